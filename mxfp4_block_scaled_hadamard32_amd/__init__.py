@@ -1,0 +1,146 @@
+"""MXFP4 block-scaled Hadamard-32 hot path for AMD MI355X (gfx950).
+
+Python face of the C ABI in include/mx.h (libmx.so). Each function marshals torch tensors (device
+memory, current HIP stream) into one library call; the quantizer, dequantizer and GEMMs all run
+in the library's HIP kernels.
+
+  mx_quantize     1x32 blocks, optional 32-point Hadamard rotation with random signs, floor or
+                  ceil E8M0 scale, RNE or Philox stochastic rounding, packed E2M1 codes
+  mx_quantize_2d  32x32 transposition-invariant blocks, plus the transposed K-major copy
+  mx_dequantize   codes * 2^(scale-127), optional inverse rotation
+  mx_gemm_fprop / mx_gemm_dgrad / mx_gemm_wgrad   block-scaled MXFP4 GEMMs, fp32 accumulate
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import (MX_BF16, MX_F32, MX_ROUND_RNE, MX_ROUND_SR, MX_SCALE_CEIL, MX_SCALE_FLOOR,
+                   MxError, check, lib, mx_quant_opts)
+
+__all__ = ["mx_quantize", "mx_quantize_2d", "mx_dequantize", "mx_gemm_fprop", "mx_gemm_dgrad",
+           "mx_gemm_wgrad", "MxError", "MX_SCALE_FLOOR", "MX_SCALE_CEIL", "MX_ROUND_RNE",
+           "MX_ROUND_SR", "lib"]
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(x: torch.Tensor) -> int:
+    if x.dtype == torch.bfloat16:
+        return MX_BF16
+    if x.dtype == torch.float32:
+        return MX_F32
+    raise TypeError("mx_quantize takes bfloat16 or float32 input")
+
+
+def _src(x: torch.Tensor):
+    if x.dim() != 2 or not x.is_cuda or x.stride(1) != 1:
+        raise ValueError("expected a 2-D CUDA tensor with contiguous rows")
+    return x.shape[0], x.shape[1], x.stride(0)
+
+
+def _opts(scale_rule, round, hadamard, sign_mask, seed) -> mx_quant_opts:
+    return mx_quant_opts(int(scale_rule), int(round), int(hadamard), int(sign_mask) & 0xFFFFFFFF,
+                         int(seed) & 0xFFFFFFFFFFFFFFFF)
+
+
+def mx_quantize(x: torch.Tensor, axis: int = 1, scale_rule: int = MX_SCALE_FLOOR,
+                round: int = MX_ROUND_RNE, hadamard: int = 0, sign_mask: int = 0, seed: int = 0,
+                codes: torch.Tensor | None = None, scales: torch.Tensor | None = None,
+                stream=None):
+    """1x32 quantize. axis=1 -> codes [rows][cols/2], scales [rows][cols/32];
+    axis=0 -> codes [cols][rows/2], scales [cols][rows/32] (K-major layout of x^T)."""
+    rows, cols, ld = _src(x)
+    shape_c = (rows, cols // 2) if axis == 1 else (cols, rows // 2)
+    shape_s = (rows, cols // 32) if axis == 1 else (cols, rows // 32)
+    if codes is None:
+        codes = torch.empty(shape_c, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(shape_s, dtype=torch.uint8, device=x.device)
+    o = _opts(scale_rule, round, hadamard, sign_mask, seed)
+    check(lib().mx_quantize(_ptr(x), _dtype_code(x), rows, cols, ld, int(axis), ctypes.byref(o),
+                            _ptr(codes), _ptr(scales), _stream(stream)), "mx_quantize")
+    return codes, scales
+
+
+def mx_quantize_2d(x: torch.Tensor, scale_rule: int = MX_SCALE_CEIL, round: int = MX_ROUND_RNE,
+                   seed: int = 0, transposed: bool = True, codes=None, scales=None, codes_t=None,
+                   scales_t=None, stream=None):
+    """32x32 quantize -> (codes [rows][cols/2], scales [rows/32][cols/32],
+    codes_t [cols][rows/2], scales_t [cols/32][rows/32]); the last two are None unless
+    transposed."""
+    rows, cols, ld = _src(x)
+    dev = x.device
+    if codes is None:
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((rows // 32, cols // 32), dtype=torch.uint8, device=dev)
+    if transposed:
+        if codes_t is None:
+            codes_t = torch.empty((cols, rows // 2), dtype=torch.uint8, device=dev)
+        if scales_t is None:
+            scales_t = torch.empty((cols // 32, rows // 32), dtype=torch.uint8, device=dev)
+    o = _opts(scale_rule, round, 0, 0, seed)
+    check(lib().mx_quantize_2d(_ptr(x), _dtype_code(x), rows, cols, ld, ctypes.byref(o),
+                               _ptr(codes), _ptr(scales), _ptr(codes_t), _ptr(scales_t),
+                               _stream(stream)), "mx_quantize_2d")
+    return codes, scales, codes_t, scales_t
+
+
+def mx_dequantize(codes: torch.Tensor, scales: torch.Tensor, rows: int, cols: int,
+                  block_rows: int = 1, inv_hadamard: int = 0, sign_mask: int = 0,
+                  out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.float32, device=codes.device)
+    check(lib().mx_dequantize(_ptr(codes), _ptr(scales), rows, cols, int(block_rows),
+                              int(inv_hadamard), int(sign_mask) & 0xFFFFFFFF, _ptr(out),
+                              _stream(stream)), "mx_dequantize")
+    return out
+
+
+def _out(out, rows, cols, out_dtype, device):
+    if out is None:
+        out = torch.empty((rows, cols), dtype=out_dtype, device=device)
+    code = MX_BF16 if out.dtype == torch.bfloat16 else MX_F32
+    if out.dtype not in (torch.bfloat16, torch.float32) or out.stride(1) != 1:
+        raise ValueError("output must be bf16 or fp32 with contiguous rows")
+    return out, code
+
+
+def _gemm(name, aq, as_, ga, bq, bs, gb, alpha_exp, out_dtype, out, stream):
+    M, K = aq.shape[0], 2 * aq.shape[1]
+    N = bq.shape[0]
+    if 2 * bq.shape[1] != K:
+        raise ValueError("operands disagree on the reduction length")
+    out, code = _out(out, M, N, out_dtype, aq.device)
+    check(getattr(lib(), name)(_ptr(aq), _ptr(as_), int(ga), _ptr(bq), _ptr(bs), int(gb), M, N, K,
+                               int(alpha_exp), code, _ptr(out), out.stride(0), _stream(stream)),
+          name)
+    return out
+
+
+def mx_gemm_fprop(xq, xs, gx, wq, ws, gw, alpha_exp=0, out_dtype=torch.bfloat16, out=None,
+                  stream=None):
+    """Y[T][N] = 2^alpha sum_k X[t][k] W[n][k]; xq [T][K/2], wq [N][K/2]."""
+    return _gemm("mx_gemm_fprop", xq, xs, gx, wq, ws, gw, alpha_exp, out_dtype, out, stream)
+
+
+def mx_gemm_dgrad(dyq, dys, gdy, wtq, wts, gwt, alpha_exp=0, out_dtype=torch.bfloat16, out=None,
+                  stream=None):
+    """dX[T][K] = 2^alpha sum_n dY[t][n] Wt[k][n]; dyq [T][N/2], wtq [K][N/2]."""
+    return _gemm("mx_gemm_dgrad", dyq, dys, gdy, wtq, wts, gwt, alpha_exp, out_dtype, out, stream)
+
+
+def mx_gemm_wgrad(dytq, dyts, gdy, xtq, xts, gx, alpha_exp=0, out_dtype=torch.bfloat16, out=None,
+                  stream=None):
+    """dW[N][K] = 2^alpha sum_t dYt[n][t] Xt[k][t]; dytq [N][T/2], xtq [K][T/2]."""
+    return _gemm("mx_gemm_wgrad", dytq, dyts, gdy, xtq, xts, gx, alpha_exp, out_dtype, out, stream)

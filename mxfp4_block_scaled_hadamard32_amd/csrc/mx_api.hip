@@ -1,0 +1,139 @@
+// mx_api.hip — the extern "C" entry points declared in include/mx.h: argument validation and
+// dispatch to the kernel launchers. No allocation, no synchronisation, no global state.
+#include "mx.h"
+#include "mx_launch.h"
+
+namespace {
+
+constexpr int32_t kVersion = 100;  // 0.1.0
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+mx_status launch_status(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_LAUNCH; }
+
+mx_status check_opts(const mx_quant_opts* o) {
+  if (!o) return MX_ERR_NULL;
+  if (o->scale_rule != MX_SCALE_FLOOR && o->scale_rule != MX_SCALE_CEIL) return MX_ERR_ARG;
+  if (o->round != MX_ROUND_RNE && o->round != MX_ROUND_SR) return MX_ERR_ARG;
+  if (o->hadamard != 0 && o->hadamard != 1) return MX_ERR_ARG;
+  return MX_OK;
+}
+
+// Source tensor checks shared by both quantizers: rows 16-byte aligned (8 elements per lane).
+mx_status check_source(const void* x, int32_t dtype, int64_t rows, int64_t cols, int64_t ld) {
+  if (dtype != MX_F32 && dtype != MX_BF16) return MX_ERR_ARG;
+  if (rows < 0 || cols < 0 || ld < cols) return MX_ERR_SHAPE;
+  const int64_t esize = dtype == MX_BF16 ? 2 : 4;
+  if ((ld * esize) % 16 != 0) return MX_ERR_SHAPE;
+  if (!aligned(x, 16)) return MX_ERR_ARG;
+  return MX_OK;
+}
+
+mx_status gemm(const uint8_t* a, const uint8_t* as, int32_t ga, const uint8_t* b,
+               const uint8_t* bs, int32_t gb, int64_t M, int64_t N, int64_t K, int32_t alpha_exp,
+               int32_t out_dtype, void* c, int64_t ldc, void* stream) {
+  if (M < 0 || N < 0 || K < 0) return MX_ERR_SHAPE;
+  if (M % 32 || N % 32 || K % 32) return MX_ERR_SHAPE;
+  if (ldc < N || ldc % 8 != 0) return MX_ERR_SHAPE;
+  if ((ga != 1 && ga != 32) || (gb != 1 && gb != 32)) return MX_ERR_ARG;
+  if (out_dtype != MX_F32 && out_dtype != MX_BF16) return MX_ERR_ARG;
+  if (alpha_exp < -126 || alpha_exp > 127) return MX_ERR_ARG;
+  if (M == 0 || N == 0) return MX_OK;
+  if (!c) return MX_ERR_NULL;
+  if (!aligned(c, 16)) return MX_ERR_ARG;
+  if (K > 0) {
+    if (!a || !as || !b || !bs) return MX_ERR_NULL;
+    if (!aligned(a, 16) || !aligned(b, 16)) return MX_ERR_ARG;
+  }
+  GemmArgs g{a, as, ga, b, bs, gb, M, N, K, alpha_exp, out_dtype == MX_BF16, c, ldc, stream};
+  return launch_status(mx_launch_gemm(g));
+}
+
+}  // namespace
+
+extern "C" {
+
+mx_status mx_quantize(const void* x, int32_t dtype, int64_t rows, int64_t cols, int64_t ld,
+                      int32_t axis, const mx_quant_opts* opts, uint8_t* codes, uint8_t* scales,
+                      void* stream) {
+  mx_status s = check_opts(opts);
+  if (s != MX_OK) return s;
+  if (axis != 0 && axis != 1) return MX_ERR_ARG;
+  if ((s = check_source(x, dtype, rows, cols, ld)) != MX_OK) return s;
+  if (axis == 1 && cols % 32 != 0) return MX_ERR_SHAPE;
+  if (axis == 0 && (rows % 32 != 0 || cols % 8 != 0)) return MX_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return MX_OK;
+  if (!x || !codes || !scales) return MX_ERR_NULL;
+  if (!aligned(codes, 4)) return MX_ERR_ARG;
+  QuantArgs a{x, dtype == MX_BF16, rows, cols, ld, axis, opts->scale_rule == MX_SCALE_CEIL,
+              opts->round == MX_ROUND_SR, opts->hadamard == 1, opts->sign_mask, opts->seed,
+              codes, scales, nullptr, nullptr, stream};
+  return launch_status(mx_launch_quantize(a));
+}
+
+mx_status mx_quantize_2d(const void* x, int32_t dtype, int64_t rows, int64_t cols, int64_t ld,
+                         const mx_quant_opts* opts, uint8_t* codes, uint8_t* scales,
+                         uint8_t* codes_t, uint8_t* scales_t, void* stream) {
+  mx_status s = check_opts(opts);
+  if (s != MX_OK) return s;
+  if (opts->hadamard) return MX_ERR_UNSUPPORTED;
+  if ((s = check_source(x, dtype, rows, cols, ld)) != MX_OK) return s;
+  if (rows % 32 != 0 || cols % 32 != 0) return MX_ERR_SHAPE;
+  if ((codes_t == nullptr) != (scales_t == nullptr)) return MX_ERR_NULL;
+  if (rows == 0 || cols == 0) return MX_OK;
+  if (!x || !codes || !scales) return MX_ERR_NULL;
+  if (!aligned(codes, 4) || (codes_t && !aligned(codes_t, 4))) return MX_ERR_ARG;
+  QuantArgs a{x, dtype == MX_BF16, rows, cols, ld, 1, opts->scale_rule == MX_SCALE_CEIL,
+              opts->round == MX_ROUND_SR, false, 0u, opts->seed, codes, scales, codes_t,
+              scales_t, stream};
+  return launch_status(mx_launch_quantize_2d(a));
+}
+
+mx_status mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                        int32_t block_rows, int32_t inv_hadamard, uint32_t sign_mask, float* out,
+                        void* stream) {
+  if (rows < 0 || cols < 0 || cols % 32 != 0) return MX_ERR_SHAPE;
+  if (block_rows != 1 && block_rows != 32) return MX_ERR_ARG;
+  if (inv_hadamard != 0 && inv_hadamard != 1) return MX_ERR_ARG;
+  if (inv_hadamard && block_rows != 1) return MX_ERR_UNSUPPORTED;
+  if (block_rows == 32 && rows % 32 != 0) return MX_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return MX_OK;
+  if (!codes || !scales || !out) return MX_ERR_NULL;
+  if (!aligned(codes, 4) || !aligned(out, 16)) return MX_ERR_ARG;
+  return launch_status(mx_launch_dequantize(codes, scales, rows, cols, block_rows, inv_hadamard,
+                                            sign_mask, out, stream));
+}
+
+mx_status mx_gemm_fprop(const uint8_t* xq, const uint8_t* xs, int32_t gx, const uint8_t* wq,
+                        const uint8_t* ws, int32_t gw, int64_t T, int64_t N, int64_t K,
+                        int32_t alpha_exp, int32_t out_dtype, void* y, int64_t ldy, void* stream) {
+  return gemm(xq, xs, gx, wq, ws, gw, T, N, K, alpha_exp, out_dtype, y, ldy, stream);
+}
+
+mx_status mx_gemm_dgrad(const uint8_t* dyq, const uint8_t* dys, int32_t gdy, const uint8_t* wtq,
+                        const uint8_t* wts, int32_t gwt, int64_t T, int64_t K, int64_t N,
+                        int32_t alpha_exp, int32_t out_dtype, void* dx, int64_t ldx, void* stream) {
+  return gemm(dyq, dys, gdy, wtq, wts, gwt, T, K, N, alpha_exp, out_dtype, dx, ldx, stream);
+}
+
+mx_status mx_gemm_wgrad(const uint8_t* dytq, const uint8_t* dyts, int32_t gdy, const uint8_t* xtq,
+                        const uint8_t* xts, int32_t gx, int64_t N, int64_t K, int64_t T,
+                        int32_t alpha_exp, int32_t out_dtype, void* dw, int64_t ldw, void* stream) {
+  return gemm(dytq, dyts, gdy, xtq, xts, gx, N, K, T, alpha_exp, out_dtype, dw, ldw, stream);
+}
+
+const char* mx_status_string(int32_t status) {
+  switch (status) {
+    case MX_OK: return "MX_OK";
+    case MX_ERR_NULL: return "MX_ERR_NULL: a required pointer is NULL";
+    case MX_ERR_SHAPE: return "MX_ERR_SHAPE: bad dimension, multiple-of-32 rule or leading dimension";
+    case MX_ERR_UNSUPPORTED: return "MX_ERR_UNSUPPORTED: option combination not defined";
+    case MX_ERR_LAUNCH: return "MX_ERR_LAUNCH: the HIP runtime refused the launch";
+    case MX_ERR_ARG: return "MX_ERR_ARG: option value out of range or misaligned pointer";
+    default: return "unknown mx_status";
+  }
+}
+
+int32_t mx_version(void) { return kVersion; }
+
+}  // extern "C"

@@ -1,0 +1,193 @@
+// mx_device.h — device-side building blocks of the gfx950 MXFP4 path (quantize and GEMM
+// kernels include it; it is not part of the C ABI).
+//
+// Pages, cited by title and section:
+//  [P1] "Block-Scaled MXFP4 With Stochastic Hadamard Rounding Matches BF16 Convergence on 70B
+//       Pre-Training", paragraphs 1-2 (E8M0 per 32 E2M1 values; 32-point Walsh-Hadamard in
+//       registers before packing to 4 bits).
+//  [P3] "Stable FP4 Training via Transposition-Invariant Block Quantization", sections "Why FP4
+//       training is the current frontier" (E2M1; scale from the block maximum) and "The fix,
+//       and its supporting cast" (power-of-two scale rounded up; stochastic rounding).
+//  [P4] "Training LLMs with MXFP4", abstract (stochastic rounding, random Hadamard signs).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxd {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------------------------
+// lane exchange inside a quad (4 consecutive lanes) through DPP quad_perm
+// ---------------------------------------------------------------------------------------------
+constexpr int kQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kRowRor4 = 0x124;  // rotate right by 4 within a row of 16 lanes
+constexpr int kRowRor8 = 0x128;  // rotate right by 8 within a row of 16 lanes
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+}
+
+// ---------------------------------------------------------------------------------------------
+// widening: bf16 -> fp32 is exact (the bf16 bits are the high half of the fp32 bits)
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ void widen_bf16x8(const u32x4 raw, float (&v)[8]) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// 32-point Walsh-Hadamard transform [P1 paragraph 2], unnormalised, natural order: butterfly
+// stages of span 1, 2, 4 inside a lane's 8 values, then span 8 and 16 across the lanes of a
+// quad (lane bit 0 carries span 8, lane bit 1 carries span 16). Each output of a stage is one
+// fp32 add or subtract of the two stage inputs, so the result does not depend on which lane
+// computes it.
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ void fwht8_inlane(float (&v)[8]) {
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i & h) continue;
+      const float a = v[i], b = v[i + h];
+      v[i] = a + b;
+      v[i + h] = a - b;
+    }
+  }
+}
+
+// Cross-lane stage: the lane whose quad bit is clear computes own + partner, the other
+// partner - own (its own value is the stage's second operand). upper_sign is 0x80000000 on the
+// lanes with the bit set, 0 otherwise.
+template <int CTRL>
+__device__ __forceinline__ float butterfly_xlane(float own, uint32_t upper_sign) {
+  const float partner = dpp_f32<CTRL>(own);
+  return partner + __uint_as_float(__float_as_uint(own) ^ upper_sign);
+}
+
+// ---------------------------------------------------------------------------------------------
+// E8M0 scale byte from the block maximum's bits [P1 paragraph 1; P3 "The fix ..."].
+// amax_bits: bits of a non-negative float. With exponent field F (amax = m * 2^(F-127)):
+//   floor: e = F - 127 - 2;  ceil: e += 1 when the mantissa exceeds 1.5.
+// byte = e + 127 clamped to [0, 254] (F = 0, i.e. zero or subnormal amax, gives byte 0);
+// a non-finite amax gives 0xFF.
+// ---------------------------------------------------------------------------------------------
+template <bool CEIL>
+__device__ __forceinline__ uint32_t scale_byte(uint32_t amax_bits) {
+  if (amax_bits >= 0x7F800000u) return 0xFFu;
+  int32_t b = (int32_t)(amax_bits >> 23) - 2;
+  if (CEIL) b += (amax_bits & 0x7FFFFFu) > 0x400000u ? 1 : 0;
+  b = b < 0 ? 0 : b;
+  return (uint32_t)b;  // F <= 254 -> b <= 253
+}
+
+// 2^-e for a finite scale byte: (254 - byte) << 23 is a normal float for byte <= 253.
+__device__ __forceinline__ float inv_scale_from_byte(uint32_t byte) {
+  return __uint_as_float((254u - byte) << 23);
+}
+
+// ---------------------------------------------------------------------------------------------
+// E2M1 rounding.
+// RNE: gfx950's converter (v_cvt_scalef32_pk_fp4_f32) with unit scale rounds to nearest with
+//      ties to the even code, saturates at 6 and copies the sign, as the definition requires.
+// SR : in software. a = min(|v|, 6); the grid step q around a is 0.5 below 2 and 2^(E-1) above
+//      (E = exponent of a); t = a / q is exact, lo index = floor(t), f = t - floor(t), and the
+//      magnitude rounds up iff r < f * 65536 with r the element's 16-bit random field.
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t cvt_rne_pack8(const float (&v)[8]) {
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], 1.0f, 3);
+  return w;
+}
+
+__device__ __forceinline__ uint32_t e2m1_sr_code(float v, uint32_t r16) {
+  const float a = fminf(fabsf(v), 6.0f);
+  const uint32_t ub = __float_as_uint(a);
+  int32_t qb = (int32_t)(ub & 0x7F800000u) - 0x00800000;
+  qb = qb > 0x3F000000 ? qb : 0x3F000000;             // step 2^(E-1), at least 0.5
+  const float inv_q = __uint_as_float(0x7F000000u - (uint32_t)qb);
+  const float t = a * inv_q;                           // exact
+  const float fl = floorf(t);
+  const float fr = t - fl;                             // exact
+  const uint32_t up = ((float)r16 < fr * 65536.0f) ? 1u : 0u;
+  const uint32_t idx = (uint32_t)fl + up + ((uint32_t)qb >> 22) - 252u;
+  return idx | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): 10 rounds of two 32x32->64 products of
+// counter words 0 and 2 with the Philox multipliers, mixed with words 1, 3 and the key; the key
+// advances by the Weyl constants between rounds. Returns the 128-bit output.
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                               uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return make_uint4(c0, c1, c2, c3);
+}
+
+// Eight 16-bit random fields for source elements 8g .. 8g+7 (field k for element 8g + k).
+__device__ __forceinline__ void sr_fields8(uint64_t g, uint64_t seed, uint32_t (&r)[8]) {
+  const uint4 w = philox4x32_10((uint32_t)g, (uint32_t)(g >> 32), 0u, 0u, (uint32_t)seed,
+                                (uint32_t)(seed >> 32));
+  r[0] = w.x & 0xFFFFu; r[1] = w.x >> 16;
+  r[2] = w.y & 0xFFFFu; r[3] = w.y >> 16;
+  r[4] = w.z & 0xFFFFu; r[5] = w.z >> 16;
+  r[6] = w.w & 0xFFFFu; r[7] = w.w >> 16;
+}
+
+// ---------------------------------------------------------------------------------------------
+// in-lane transpose of an 8x8 matrix of nibbles: R[j] nibble k -> R[k] nibble j
+// (swap 4x4 quadrants, then 2x2 sub-blocks, then single nibbles)
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ void transpose_nibbles8x8(uint32_t (&R)[8]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {  // quadrants: bytes {a0,a1,b0,b1} and {a2,a3,b2,b3}
+    const uint32_t a = R[j], b = R[j + 4];
+    R[j] = __builtin_amdgcn_perm(b, a, 0x05040100u);
+    R[j + 4] = __builtin_amdgcn_perm(b, a, 0x07060302u);
+  }
+#pragma unroll
+  for (int base = 0; base < 8; base += 4) {  // 2x2 blocks: bytes {a0,b0,a2,b2} and {a1,b1,a3,b3}
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t a = R[base + j], b = R[base + j + 2];
+      R[base + j] = __builtin_amdgcn_perm(b, a, 0x06020400u);
+      R[base + j + 2] = __builtin_amdgcn_perm(b, a, 0x07030501u);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; j += 2) {  // single nibbles
+    const uint32_t a = R[j], b = R[j + 1];
+    R[j] = (a & 0x0F0F0F0Fu) | ((b << 4) & 0xF0F0F0F0u);
+    R[j + 1] = ((a >> 4) & 0x0F0F0F0Fu) | (b & 0xF0F0F0F0u);
+  }
+}
+
+}  // namespace mxd

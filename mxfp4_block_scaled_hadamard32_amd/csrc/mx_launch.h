@@ -1,0 +1,46 @@
+// mx_launch.h — internal interface between the C ABI layer (mx_api.hip) and the kernel
+// launchers (quant.hip, gemm.hip). Arguments are already validated when these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+struct QuantArgs {
+  const void* x;
+  bool bf16;
+  int64_t rows, cols, ld;
+  int axis;          // 1D only
+  bool ceil, sr, hadamard;
+  uint32_t sign_mask;
+  uint64_t seed;
+  uint8_t* codes;    // axis 1 / 2-D: [rows][cols/2];  axis 0: [cols][rows/2]
+  uint8_t* scales;
+  uint8_t* codes_t;  // 2-D only, nullable
+  uint8_t* scales_t; // 2-D only, nullable
+  void* stream;
+};
+
+hipError_t mx_launch_quantize(const QuantArgs& a);
+hipError_t mx_launch_quantize_2d(const QuantArgs& a);
+hipError_t mx_launch_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                                int64_t cols, int block_rows, int inv_had, uint32_t sign_mask,
+                                float* out, void* stream);
+
+// C[m][n] = 2^alpha * sum_k A[m][k] * B[n][k]; A [M][K/2], B [N][K/2] packed E2M1, scales
+// [M/ga][K/32] and [N/gb][K/32].
+struct GemmArgs {
+  const uint8_t* a;
+  const uint8_t* as;
+  int ga;
+  const uint8_t* b;
+  const uint8_t* bs;
+  int gb;
+  int64_t M, N, K;
+  int alpha;
+  bool out_bf16;
+  void* c;
+  int64_t ldc;
+  void* stream;
+};
+
+hipError_t mx_launch_gemm(const GemmArgs& g);

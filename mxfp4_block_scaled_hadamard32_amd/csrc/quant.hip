@@ -1,0 +1,417 @@
+// quant.hip — MXFP4 quantize (1x32 along rows, 1x32 along columns, 32x32 tiles) and dequantize
+// kernels for gfx950, plus their host-side launchers.
+//
+// Pages, cited by title and section:
+//  [P1] "Block-Scaled MXFP4 With Stochastic Hadamard Rounding Matches BF16 Convergence on 70B
+//       Pre-Training", paragraphs 1-2: one E8M0 exponent per 32 E2M1 values; the 32-element
+//       Walsh-Hadamard rotation runs in registers before the codes are packed.
+//  [P3] "Stable FP4 Training via Transposition-Invariant Block Quantization": "Why FP4 training
+//       is the current frontier" (P = round(X/S), reconstruction P*S), "The aha: transposition
+//       scrambles the blocks" (a transposed operand is re-blocked along the other axis), "The
+//       fix, and its supporting cast" (32x32 tiles shared by X and X^T, scale rounded up so
+//       nothing clips, stochastic rounding).
+//  [P4] "Training LLMs with MXFP4", abstract: random Hadamard signs with stochastic rounding.
+//
+// Work mapping (all kernels are HBM streams):
+//  * A lane owns 8 consecutive elements of a row (one 16-byte bf16 load). Along rows, a quad of
+//    4 lanes holds one 32-block: butterfly spans 1, 2, 4 stay in the lane, spans 8 and 16 use
+//    DPP quad permutes; the block maximum reduces the same way.
+//  * Along columns and for 32x32 tiles, a lane owns an 8x8 patch (8 rows of 16 bytes). A quad
+//    stacks 4 patches into 32 rows, so the same in-lane + quad structure runs down the columns;
+//    16 lanes (4 quads side by side) make one 32x32 tile.
+//  * Stochastic rounding draws one Philox4x32-10 call per 8 consecutive source elements.
+#include "mx_device.h"
+#include "mx_launch.h"
+
+namespace {
+
+using namespace mxd;
+
+constexpr int kThreads = 256;
+constexpr int kRowChunksPerThread = 2;
+
+template <bool BF16>
+__device__ __forceinline__ void load8(const void* __restrict__ x, int64_t off, float (&v)[8]) {
+  if (BF16) {
+    const u32x4 raw = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(x) + off));
+    widen_bf16x8(raw, v);
+  } else {
+    const f32x4* p = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(x) + off);
+    const f32x4 a = __builtin_nontemporal_load(p);
+    const f32x4 b = __builtin_nontemporal_load(p + 1);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+__device__ __forceinline__ uint32_t abs_bits(float v) { return __float_as_uint(v) & 0x7FFFFFFFu; }
+
+// ---------------------------------------------------------------------------------------------
+// 1x32 blocks along rows. Chunk g = 8 consecutive elements, row-major over the logical tensor,
+// so element index 8g + k is also the stochastic-rounding index.
+// ---------------------------------------------------------------------------------------------
+template <bool BF16, bool HAD, bool SR, bool CEIL>
+__global__ __launch_bounds__(kThreads) void quant_rows_kernel(
+    const void* __restrict__ x, int64_t nchunks, int64_t cpr, int64_t ld, int contiguous,
+    uint32_t sign_mask, uint64_t seed, uint32_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const int q = threadIdx.x & 3;
+  uint32_t sgn[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) sgn[k] = HAD ? (((sign_mask >> (8 * q + k)) & 1u) << 31) : 0u;
+  const uint32_t up8 = (q & 1) ? 0x80000000u : 0u;
+  const uint32_t up16 = (q & 2) ? 0x80000000u : 0u;
+
+  const int64_t base = (int64_t)blockIdx.x * (kThreads * kRowChunksPerThread) + threadIdx.x;
+  float v[kRowChunksPerThread][8];
+#pragma unroll
+  for (int u = 0; u < kRowChunksPerThread; ++u) {
+    const int64_t g = base + (int64_t)u * kThreads;
+    if (g < nchunks) {
+      int64_t off = 8 * g;
+      if (!contiguous) {
+        const int64_t r = g / cpr;
+        off = r * ld + 8 * (g - r * cpr);
+      }
+      load8<BF16>(x, off, v[u]);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kRowChunksPerThread; ++u) {
+    const int64_t g = base + (int64_t)u * kThreads;
+    if (g >= nchunks) continue;  // quads are all in or all out (cols % 32 == 0)
+    float (&w)[8] = v[u];
+    if (HAD) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) w[k] = __uint_as_float(__float_as_uint(w[k]) ^ sgn[k]);
+      fwht8_inlane(w);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) w[k] = butterfly_xlane<kQuadXor1>(w[k], up8);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) w[k] = butterfly_xlane<kQuadXor2>(w[k], up16);
+    }
+    uint32_t m = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) m = max(m, abs_bits(w[k]));
+    m = max(m, dpp_u32<kQuadXor1>(m));
+    m = max(m, dpp_u32<kQuadXor2>(m));
+    const uint32_t sb = scale_byte<CEIL>(m);
+    uint32_t word = 0;
+    if (sb != 0xFFu) {
+      const float inv = inv_scale_from_byte(sb);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) w[k] = w[k] * inv;
+      if (SR) {
+        uint32_t r[8];
+        sr_fields8((uint64_t)g, seed, r);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) word |= e2m1_sr_code(w[k], r[k]) << (4 * k);
+      } else {
+        word = cvt_rne_pack8(w);
+      }
+    }
+    __builtin_nontemporal_store(word, codes + g);
+    if (q == 0) scales[g >> 2] = (uint8_t)sb;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// 8x8 patch loader shared by the column and 2-D kernels: rows r0..r0+7, columns c0..c0+7.
+// p[j][k] = x[r0 + j][c0 + k].
+// ---------------------------------------------------------------------------------------------
+template <bool BF16>
+__device__ __forceinline__ void load_patch(const void* __restrict__ x, int64_t ld, int64_t r0,
+                                           int64_t c0, float (&p)[8][8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) load8<BF16>(x, (r0 + j) * ld + c0, p[j]);
+}
+
+// Column transform of a patch stack: position 8q + j of the 32-block is patch row j of quad
+// lane q. Negate the rows selected by sign_mask, then the five butterfly stages per column.
+__device__ __forceinline__ void fwht_columns(float (&p)[8][8], uint32_t sign_mask, int q) {
+  const uint32_t up8 = (q & 1) ? 0x80000000u : 0u;
+  const uint32_t up16 = (q & 2) ? 0x80000000u : 0u;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t s = ((sign_mask >> (8 * q + j)) & 1u) << 31;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) p[j][k] = __uint_as_float(__float_as_uint(p[j][k]) ^ s);
+  }
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j & h) continue;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float a = p[j][k], b = p[j + h][k];
+        p[j][k] = a + b;
+        p[j + h][k] = a - b;
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) p[j][k] = butterfly_xlane<kQuadXor1>(p[j][k], up8);
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) p[j][k] = butterfly_xlane<kQuadXor2>(p[j][k], up16);
+}
+
+// ---------------------------------------------------------------------------------------------
+// 1x32 blocks down the columns (blocks along rows), output in the layout of the transpose:
+// codes_t [cols][rows/2], scales_t [cols][rows/32]. Wave w of block (bx, by) handles row block
+// rb = 4 * by + w and columns 128 * bx .. + 127; lane = 4 * column-group + q.
+// ---------------------------------------------------------------------------------------------
+template <bool BF16, bool HAD, bool SR, bool CEIL>
+__global__ __launch_bounds__(kThreads) void quant_cols_kernel(
+    const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, uint32_t sign_mask,
+    uint64_t seed, uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t) {
+  const int lane = threadIdx.x & 63;
+  const int q = lane & 3;
+  const int64_t rb = (int64_t)blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int64_t c0 = (int64_t)blockIdx.x * 128 + (lane >> 2) * 8;
+  if (rb >= rows / 32 || c0 >= cols) return;  // whole quads leave together
+  const int64_t r0 = rb * 32 + 8 * q;
+
+  float p[8][8];
+  load_patch<BF16>(x, ld, r0, c0, p);
+  if (HAD) fwht_columns(p, sign_mask, q);
+
+  uint32_t sb[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = max(m, abs_bits(p[j][k]));
+    m = max(m, dpp_u32<kQuadXor1>(m));
+    m = max(m, dpp_u32<kQuadXor2>(m));
+    sb[k] = scale_byte<CEIL>(m);
+  }
+  uint32_t r[8][8];
+  if (SR) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sr_fields8((uint64_t)((r0 + j) * cols + c0) >> 3, seed, r[j]);
+  }
+  const int64_t rows2 = rows / 2;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    uint32_t word = 0;
+    if (sb[k] != 0xFFu) {
+      const float inv = inv_scale_from_byte(sb[k]);
+      float col[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) col[j] = p[j][k] * inv;
+      if (SR) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) word |= e2m1_sr_code(col[j], r[j][k]) << (4 * j);
+      } else {
+        word = cvt_rne_pack8(col);
+      }
+    }
+    uint32_t* dst = reinterpret_cast<uint32_t*>(codes_t + (c0 + k) * rows2 + rb * 16 + 4 * q);
+    __builtin_nontemporal_store(word, dst);
+  }
+  if (q == 0) {
+    const int64_t nb = rows / 32;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) scales_t[(c0 + k) * nb + rb] = (uint8_t)sb[k];
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// 32x32 tiles: one scale per tile from the tile maximum; every element is rounded once and
+// written to the row-major codes and (optionally) to the K-major codes of the transpose.
+// Lane = 16 * tile + 4 * column-group + q; the 16 lanes of a tile are one DPP row.
+// ---------------------------------------------------------------------------------------------
+template <bool BF16, bool SR, bool CEIL>
+__global__ __launch_bounds__(kThreads) void quant_2d_kernel(
+    const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, uint64_t seed,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, uint8_t* __restrict__ codes_t,
+    uint8_t* __restrict__ scales_t) {
+  const int lane = threadIdx.x & 63;
+  const int q = lane & 3;
+  const int64_t rb = (int64_t)blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int64_t c0 = (int64_t)blockIdx.x * 128 + (lane >> 2) * 8;
+  if (rb >= rows / 32 || c0 >= cols) return;  // whole tiles leave together (cols % 32 == 0)
+  const int64_t r0 = rb * 32 + 8 * q;
+
+  float p[8][8];
+  load_patch<BF16>(x, ld, r0, c0, p);
+
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) m = max(m, abs_bits(p[j][k]));
+  m = max(m, dpp_u32<kQuadXor1>(m));
+  m = max(m, dpp_u32<kQuadXor2>(m));
+  m = max(m, dpp_u32<kRowRor4>(m));
+  m = max(m, dpp_u32<kRowRor8>(m));
+  const uint32_t sb = scale_byte<CEIL>(m);
+
+  uint32_t R[8];  // R[j] = codes of patch row j (nibble k = column k)
+  if (sb == 0xFFu) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) R[j] = 0;
+  } else {
+    const float inv = inv_scale_from_byte(sb);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) p[j][k] = p[j][k] * inv;
+      if (SR) {
+        uint32_t r[8];
+        sr_fields8((uint64_t)((r0 + j) * cols + c0) >> 3, seed, r);
+        uint32_t word = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) word |= e2m1_sr_code(p[j][k], r[k]) << (4 * k);
+        R[j] = word;
+      } else {
+        R[j] = cvt_rne_pack8(p[j]);
+      }
+    }
+  }
+  const int64_t cols2 = cols / 2;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    __builtin_nontemporal_store(R[j], reinterpret_cast<uint32_t*>(codes + (r0 + j) * cols2 + c0 / 2));
+  if (codes_t) {
+    transpose_nibbles8x8(R);  // R[k] = codes of patch column k (nibble j = row j)
+    const int64_t rows2 = rows / 2;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      __builtin_nontemporal_store(R[k], reinterpret_cast<uint32_t*>(codes_t + (c0 + k) * rows2 + r0 / 2));
+  }
+  if ((lane & 15) == 0) {
+    const int64_t tc = c0 / 32;
+    scales[rb * (cols / 32) + tc] = (uint8_t)sb;
+    if (scales_t) scales_t[tc * (rows / 32) + rb] = (uint8_t)sb;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Dequantize: out = E2M1(code) * 2^(byte-127) in fp32; optional inverse rotation (1/32) D H
+// per 32-block along the row. One lane per 8 elements, flat over the tensor.
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ float e2m1_value(uint32_t code) {
+  const uint32_t E = (code >> 1) & 3u, M = code & 1u;
+  const uint32_t mag = E ? (((E + 126u) << 23) | (M << 22)) : (M ? 0x3F000000u : 0u);
+  return __uint_as_float(mag | ((code & 8u) << 28));
+}
+
+__global__ __launch_bounds__(kThreads) void dequant_kernel(
+    const uint32_t* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t rows,
+    int64_t cols, int block_rows, int inv_had, uint32_t sign_mask, float* __restrict__ out) {
+  const int64_t cpr = cols / 8;
+  const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (g >= rows * cpr) return;  // quads stay whole (cols % 32 == 0)
+  const int64_t row = g / cpr;
+  const int64_t cc = g - row * cpr;
+  const uint32_t word = codes[g];
+  const uint32_t s = scales[(row / block_rows) * (cols / 32) + (cc >> 2)];
+  float v[8];
+  if (s == 0xFFu) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = __uint_as_float(0x7FC00000u);
+  } else {
+    const float p = __uint_as_float(s ? (s << 23) : 0x00400000u);  // 2^(s-127)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = e2m1_value((word >> (4 * k)) & 0xFu) * p;
+  }
+  if (inv_had) {
+    const int q = threadIdx.x & 3;
+    fwht8_inlane(v);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = butterfly_xlane<kQuadXor1>(v[k], (q & 1) ? 0x80000000u : 0u);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = butterfly_xlane<kQuadXor2>(v[k], (q & 2) ? 0x80000000u : 0u);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      v[k] = v[k] * 0.03125f;
+      v[k] = __uint_as_float(__float_as_uint(v[k]) ^ (((sign_mask >> (8 * q + k)) & 1u) << 31));
+    }
+  }
+  float4* o = reinterpret_cast<float4*>(out + 8 * g);
+  o[0] = make_float4(v[0], v[1], v[2], v[3]);
+  o[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+// ---------------------------------------------------------------------------------------------
+// host-side dispatch over the compile-time variants
+// ---------------------------------------------------------------------------------------------
+template <bool BF16, bool HAD, bool SR, bool CEIL>
+hipError_t launch_rows(const QuantArgs& a) {
+  const int64_t cpr = a.cols / 8;
+  const int64_t nchunks = a.rows * cpr;
+  const int64_t per_block = kThreads * kRowChunksPerThread;
+  const int64_t nblocks = (nchunks + per_block - 1) / per_block;
+  if (nblocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((quant_rows_kernel<BF16, HAD, SR, CEIL>), dim3((unsigned)nblocks), dim3(kThreads),
+                     0, (hipStream_t)a.stream, a.x, nchunks, cpr, a.ld, a.ld == a.cols ? 1 : 0,
+                     a.sign_mask, a.seed, reinterpret_cast<uint32_t*>(a.codes), a.scales);
+  return hipGetLastError();
+}
+
+template <bool BF16, bool HAD, bool SR, bool CEIL>
+hipError_t launch_cols(const QuantArgs& a) {
+  const dim3 grid((unsigned)((a.cols + 127) / 128), (unsigned)((a.rows / 32 + 3) / 4));
+  if (grid.y > 65535u) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((quant_cols_kernel<BF16, HAD, SR, CEIL>), grid, dim3(kThreads), 0,
+                     (hipStream_t)a.stream, a.x, a.rows, a.cols, a.ld, a.sign_mask, a.seed,
+                     a.codes, a.scales);
+  return hipGetLastError();
+}
+
+template <bool BF16, bool SR, bool CEIL>
+hipError_t launch_2d(const QuantArgs& a) {
+  const dim3 grid((unsigned)((a.cols + 127) / 128), (unsigned)((a.rows / 32 + 3) / 4));
+  if (grid.y > 65535u) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((quant_2d_kernel<BF16, SR, CEIL>), grid, dim3(kThreads), 0,
+                     (hipStream_t)a.stream, a.x, a.rows, a.cols, a.ld, a.seed, a.codes, a.scales,
+                     a.codes_t, a.scales_t);
+  return hipGetLastError();
+}
+
+template <bool BF16, bool HAD, bool SR>
+hipError_t pick_rule_1d(const QuantArgs& a) {
+  if (a.axis == 1)
+    return a.ceil ? launch_rows<BF16, HAD, SR, true>(a) : launch_rows<BF16, HAD, SR, false>(a);
+  return a.ceil ? launch_cols<BF16, HAD, SR, true>(a) : launch_cols<BF16, HAD, SR, false>(a);
+}
+
+template <bool BF16>
+hipError_t pick_1d(const QuantArgs& a) {
+  if (a.hadamard)
+    return a.sr ? pick_rule_1d<BF16, true, true>(a) : pick_rule_1d<BF16, true, false>(a);
+  return a.sr ? pick_rule_1d<BF16, false, true>(a) : pick_rule_1d<BF16, false, false>(a);
+}
+
+template <bool BF16>
+hipError_t pick_2d(const QuantArgs& a) {
+  if (a.sr) return a.ceil ? launch_2d<BF16, true, true>(a) : launch_2d<BF16, true, false>(a);
+  return a.ceil ? launch_2d<BF16, false, true>(a) : launch_2d<BF16, false, false>(a);
+}
+
+}  // namespace
+
+hipError_t mx_launch_quantize(const QuantArgs& a) {
+  return a.bf16 ? pick_1d<true>(a) : pick_1d<false>(a);
+}
+
+hipError_t mx_launch_quantize_2d(const QuantArgs& a) {
+  return a.bf16 ? pick_2d<true>(a) : pick_2d<false>(a);
+}
+
+hipError_t mx_launch_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                                int64_t cols, int block_rows, int inv_had, uint32_t sign_mask,
+                                float* out, void* stream) {
+  const int64_t nblocks = (rows * (cols / 8) + kThreads - 1) / kThreads;
+  if (nblocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)nblocks), dim3(kThreads), 0, (hipStream_t)stream,
+                     reinterpret_cast<const uint32_t*>(codes), scales, rows, cols, block_rows,
+                     inv_had, sign_mask, out);
+  return hipGetLastError();
+}

@@ -1,0 +1,110 @@
+"""The C ABI library loads, exports every entry point declared in include/mx.h, and rejects bad
+arguments with the documented status codes before touching the GPU (so these run on a host with
+no GPU: validation happens before any HIP call, and no pointer here is dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from mxfp4_block_scaled_hadamard32_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libmx.so not built (run __graft_entry__.build())")
+    return _lib.lib()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "mx.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mx_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert {"mx_quantize", "mx_quantize_2d", "mx_dequantize", "mx_gemm_fprop", "mx_gemm_dgrad",
+            "mx_gemm_wgrad"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings(L):
+    assert L.mx_version() >= 100
+    from mxfp4_block_scaled_hadamard32_amd import _lib
+    for s in range(6):
+        assert _lib.status_string(s).startswith("MX_")
+
+
+FAKE = ctypes.c_void_p(0x10000)  # aligned, never dereferenced on the error paths below
+
+
+def opts(**kw):
+    from mxfp4_block_scaled_hadamard32_amd._lib import mx_quant_opts
+    o = mx_quant_opts(0, 0, 0, 0, 0)
+    for k, v in kw.items():
+        setattr(o, k, v)
+    return ctypes.byref(o)
+
+
+def test_quantize_argument_errors(L):
+    from mxfp4_block_scaled_hadamard32_amd import _lib as m
+    q = L.mx_quantize
+    assert q(FAKE, 1, 64, 48, 48, 1, opts(), FAKE, FAKE, None) == m.MX_ERR_SHAPE   # cols % 32
+    assert q(FAKE, 1, 48, 64, 64, 0, opts(), FAKE, FAKE, None) == m.MX_ERR_SHAPE   # rows % 32
+    assert q(FAKE, 1, 64, 64, 32, 1, opts(), FAKE, FAKE, None) == m.MX_ERR_SHAPE   # ld < cols
+    assert q(FAKE, 1, 64, 64, 68, 1, opts(), FAKE, FAKE, None) == m.MX_ERR_SHAPE   # ld*2 % 16
+    assert q(FAKE, 7, 64, 64, 64, 1, opts(), FAKE, FAKE, None) == m.MX_ERR_ARG     # dtype
+    assert q(FAKE, 1, 64, 64, 64, 2, opts(), FAKE, FAKE, None) == m.MX_ERR_ARG     # axis
+    assert q(FAKE, 1, 64, 64, 64, 1, opts(round=5), FAKE, FAKE, None) == m.MX_ERR_ARG
+    assert q(FAKE, 1, 64, 64, 64, 1, None, FAKE, FAKE, None) == m.MX_ERR_NULL
+    assert q(None, 1, 64, 64, 64, 1, opts(), FAKE, FAKE, None) == m.MX_ERR_NULL
+    assert q(FAKE, 1, 64, 64, 64, 1, opts(), None, FAKE, None) == m.MX_ERR_NULL
+    assert q(ctypes.c_void_p(0x10008), 1, 64, 64, 64, 1, opts(), FAKE, FAKE, None) == m.MX_ERR_ARG
+    # empty tensors are fine and launch nothing
+    assert q(None, 1, 0, 64, 64, 1, opts(), None, None, None) == m.MX_OK
+    assert q(None, 1, 32, 0, 0, 0, opts(), None, None, None) == m.MX_OK
+
+
+def test_quantize_2d_argument_errors(L):
+    from mxfp4_block_scaled_hadamard32_amd import _lib as m
+    q = L.mx_quantize_2d
+    assert q(FAKE, 1, 64, 64, 64, opts(hadamard=1), FAKE, FAKE, None, None, None) == m.MX_ERR_UNSUPPORTED
+    assert q(FAKE, 1, 48, 64, 64, opts(), FAKE, FAKE, None, None, None) == m.MX_ERR_SHAPE
+    assert q(FAKE, 1, 64, 64, 64, opts(), FAKE, FAKE, FAKE, None, None) == m.MX_ERR_NULL
+    assert q(None, 1, 0, 0, 0, opts(), None, None, None, None, None) == m.MX_OK
+
+
+def test_dequantize_argument_errors(L):
+    from mxfp4_block_scaled_hadamard32_amd import _lib as m
+    d = L.mx_dequantize
+    assert d(FAKE, FAKE, 4, 48, 1, 0, 0, FAKE, None) == m.MX_ERR_SHAPE
+    assert d(FAKE, FAKE, 64, 64, 2, 0, 0, FAKE, None) == m.MX_ERR_ARG
+    assert d(FAKE, FAKE, 64, 64, 32, 1, 0, FAKE, None) == m.MX_ERR_UNSUPPORTED
+    assert d(FAKE, FAKE, 40, 64, 32, 0, 0, FAKE, None) == m.MX_ERR_SHAPE
+    assert d(None, FAKE, 64, 64, 1, 0, 0, FAKE, None) == m.MX_ERR_NULL
+    assert d(None, None, 0, 64, 1, 0, 0, None, None) == m.MX_OK
+
+
+@pytest.mark.parametrize("name", ["mx_gemm_fprop", "mx_gemm_dgrad", "mx_gemm_wgrad"])
+def test_gemm_argument_errors(L, name):
+    from mxfp4_block_scaled_hadamard32_amd import _lib as m
+    g = getattr(L, name)
+    ok = dict(M=64, N=64, K=64)
+
+    def call(M=64, N=64, K=64, ga=1, gb=1, alpha=0, dt=1, c=FAKE, ldc=64, a=FAKE):
+        return g(a, FAKE, ga, FAKE, FAKE, gb, M, N, K, alpha, dt, c, ldc, None)
+    assert call(M=48) == m.MX_ERR_SHAPE
+    assert call(K=40) == m.MX_ERR_SHAPE
+    assert call(ldc=60) == m.MX_ERR_SHAPE
+    assert call(ldc=72 + 4) == m.MX_ERR_SHAPE
+    assert call(ga=2) == m.MX_ERR_ARG
+    assert call(dt=3) == m.MX_ERR_ARG
+    assert call(alpha=200) == m.MX_ERR_ARG
+    assert call(c=None) == m.MX_ERR_NULL
+    assert call(a=None) == m.MX_ERR_NULL
+    assert call(M=0) == m.MX_OK and call(N=0, c=None) == m.MX_OK
+    del ok
