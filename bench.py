@@ -1,0 +1,268 @@
+"""Throughput of the MXFP4 block-scaled Hadamard-32 hot path on one MI355X.
+
+One step = the whole path of a linear layer over one synthetic batch: six operand quantizations
+(32-point Hadamard with random signs, truncation-free ceil scale, Philox stochastic rounding,
+each along the reduction axis of the GEMM that consumes it) and the three MXFP4 GEMMs
+(Fprop Y = H W^T, Dgrad dH = dY W, Wgrad dW = dY^T H), bf16 outputs, fp32 accumulation.
+
+Default workload: the 70B MLP down-projection, one GPU's share (T=16384 tokens, hidden 8192,
+FFN 28672). Inputs are generated on the GPU before timing (seeded, synthetic).
+
+Prints one JSON line: whole-step MXFP4 TFLOP/s (value), plus the headline components — Wgrad
+GEMM TFLOP/s and Hadamard-quantize GB/s as fractions of MI355X peak — the roofline record of the
+dominant kernel (the GEMM, timed with HIP events on its stream) and the CPU oracle baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MXFP4 Wgrad GEMM TFLOPS + Hadamard-quant GB/s, as % of MI355X peak"
+PEAK_FP4_TFLOPS = 10100.0   # MI355X dense MXFP4 matrix peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+QUANT_BYTES_PER_ELEM = 2.0 + 0.5 + 1.0 / 32.0   # bf16 read + packed code + scale byte
+GEMM_SRC = os.path.join(ROOT, "mxfp4_block_scaled_hadamard32_amd", "csrc", "gemm.hip")
+QUANT_SRC = os.path.join(ROOT, "mxfp4_block_scaled_hadamard32_amd", "csrc", "quant.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_llama70b_down.json")
+
+
+def sha(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="llama70b_down", choices=["llama70b_down", "llama8b_up"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-rows", type=int, default=256,
+                   help="source rows per operand quantization in the CPU oracle sample")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also launch one plain 1 GiB device copy (counter calibration runs)")
+    return p.parse_args()
+
+
+class Layer:
+    """Device buffers and the six quantize + three GEMM launches of one linear-layer step."""
+
+    def __init__(self, mx, wl, workload: str):
+        import torch
+        self.mx, self.torch = mx, torch
+        dev = "cuda"
+        if workload == "llama70b_down":
+            d = wl.llama70b_down(device=dev)
+            self.X, self.W, self.dY = d["H"], d["W"], d["dY"]
+            mask = wl.sign_mask()
+            # (hadamard, mask, rule, round, alpha) per GEMM
+            self.fprop_q = self.dgrad_q = self.wgrad_q = (1, mask, 1, 1)
+            self.alpha = {"fprop": -5, "dgrad": -5, "wgrad": -5}
+            self.desc = ("70B MLP down-projection, one GPU's share: H 16384x28672 ~ t(3), "
+                         "W 8192x28672 ~ N(0,0.01), dY 16384x8192 ~ N(0,1e-3), bf16; "
+                         "Hadamard32 (random signs) + ceil scale + SR on all six operand "
+                         "quantizations; Fprop/Dgrad/Wgrad bf16 out")
+        else:
+            d = wl.llama8b_up(device=dev)
+            self.X, self.W, self.dY = d["X"], d["W"], d["dY"]
+            self.fprop_q = self.dgrad_q = (0, 0, 0, 0)
+            self.wgrad_q = (1, 0, 0, 0)   # deterministic Hadamard along T, floor, RNE
+            self.alpha = {"fprop": 0, "dgrad": 0, "wgrad": -5}
+            self.desc = ("Llama-3.1-8B MLP up-projection, one GPU's share: T=8192, K=4096, "
+                         "N=14336; floor scale, RNE; Wgrad with deterministic Hadamard along T")
+        self.workload = workload
+        self.T, self.K = self.X.shape
+        self.N = self.W.shape[0]
+        self.seeds = {"X": wl.SR_SEED, "W": wl.SR_SEED + 1, "dY": wl.SR_SEED + 2}
+        T, K, N = self.T, self.K, self.N
+        u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device=dev)  # noqa: E731
+        self.buf = {
+            "Xq": (u8(T, K // 2), u8(T, K // 32)), "Wq": (u8(N, K // 2), u8(N, K // 32)),
+            "dYq": (u8(T, N // 2), u8(T, N // 32)), "Wt": (u8(K, N // 2), u8(K, N // 32)),
+            "dYt": (u8(N, T // 2), u8(N, T // 32)), "Xt": (u8(K, T // 2), u8(K, T // 32)),
+        }
+        bf = torch.bfloat16
+        self.Y = torch.empty((T, N), dtype=bf, device=dev)
+        self.dX = torch.empty((T, K), dtype=bf, device=dev)
+        self.dW = torch.empty((N, K), dtype=bf, device=dev)
+        self.flops = {"fprop": 2.0 * T * N * K, "dgrad": 2.0 * T * K * N, "wgrad": 2.0 * N * K * T}
+
+    def quant(self, name, src, axis, q, seed_key):
+        had, mask, rule, rnd = q
+        c, s = self.buf[name]
+        self.mx.mx_quantize(src, axis=axis, scale_rule=rule, round=rnd, hadamard=had,
+                            sign_mask=mask, seed=self.seeds[seed_key], codes=c, scales=s)
+
+    def step(self, ev=None):
+        mx = self.mx
+        if ev is not None:
+            ev["q0"].record()
+        self.quant("Xq", self.X, 1, self.fprop_q, "X")       # largest quantize: X along K
+        if ev is not None:
+            ev["q1"].record()
+        self.quant("Wq", self.W, 1, self.fprop_q, "W")
+        self.quant("dYq", self.dY, 1, self.dgrad_q, "dY")
+        self.quant("Wt", self.W, 0, self.dgrad_q, "W")
+        self.quant("dYt", self.dY, 0, self.wgrad_q, "dY")
+        self.quant("Xt", self.X, 0, self.wgrad_q, "X")
+        b = self.buf
+        mx.mx_gemm_fprop(*b["Xq"], 1, *b["Wq"], 1, alpha_exp=self.alpha["fprop"], out=self.Y)
+        mx.mx_gemm_dgrad(*b["dYq"], 1, *b["Wt"], 1, alpha_exp=self.alpha["dgrad"], out=self.dX)
+        if ev is not None:
+            ev["w0"].record()
+        mx.mx_gemm_wgrad(*b["dYt"], 1, *b["Xt"], 1, alpha_exp=self.alpha["wgrad"], out=self.dW)
+        if ev is not None:
+            ev["w1"].record()
+
+
+def cpu_baseline(layer, rows: int):
+    """The CPU oracle as it stands, on a bounded sample of the same step, extrapolated to the full
+    step: each of the six quantizations on its first `rows` source rows, and each GEMM on a
+    16 x 512 block of outputs. Returns the whole-step rate in TFLOP/s."""
+    import numpy as np
+    from oracle import oracle as orc
+    import workloads as wl
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    threads = max(1, min(threads, os.cpu_count() or 1, 16))
+    L = layer
+    total = 0.0
+    specs = [("X", L.X, 1, L.fprop_q), ("W", L.W, 1, L.fprop_q), ("dY", L.dY, 1, L.dgrad_q),
+             ("W", L.W, 0, L.dgrad_q), ("dY", L.dY, 0, L.wgrad_q), ("X", L.X, 0, L.wgrad_q)]
+    for key, src, axis, (had, mask, rule, rnd) in specs:
+        r = min(rows, src.shape[0])
+        r -= r % 32
+        sample = wl.host_input(src[:r])
+        t0 = time.perf_counter()
+        orc.quantize(sample, axis=axis, scale_rule=rule, round_mode=rnd, hadamard=had,
+                     sign_mask=mask, seed=L.seeds[key], nthreads=threads)
+        total += (time.perf_counter() - t0) * src.shape[0] / r
+    gm, gn = 16, 512
+    b = L.buf
+    for name, (aq, as_), (bq, bs), M, N, K in [
+            ("fprop", b["Xq"], b["Wq"], L.T, L.N, L.K), ("dgrad", b["dYq"], b["Wt"], L.T, L.K, L.N),
+            ("wgrad", b["dYt"], b["Xt"], L.N, L.K, L.T)]:
+        ha, hsa = aq[:gm].cpu().numpy(), as_[:gm].cpu().numpy()
+        hb, hsb = bq[:gn].cpu().numpy(), bs[:gn].cpu().numpy()
+        t0 = time.perf_counter()
+        orc.gemm(ha, hsa, 1, hb, hsb, 1, gm, gn, K, L.alpha[name])
+        total += (time.perf_counter() - t0) * (M * N) / (gm * gn)
+    flops = sum(L.flops.values())
+    return {"value": flops / total / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": (f"oracle quantize of the first {rows} source rows of each of the 6 operand "
+                       f"quantizations and oracle GEMM of a {gm}x{gn} output block of each GEMM, "
+                       f"times extrapolated by element count to the full step "
+                       f"(extrapolated full step {total:.1f} s)"),
+            "np_threads_note": "numpy float64 matmul uses the BLAS thread pool",
+            "_numpy": np.__version__}
+
+
+def load_traffic(launch_flops_key: str):
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = json.load(open(TRAFFIC_FILE))
+    if rec.get("gemm_sha") != sha(GEMM_SRC):
+        return None  # counters were taken on an older kernel
+    return rec.get(launch_flops_key)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the path's multi-GPU sharding is described in DESIGN.md, not built)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import mxfp4_block_scaled_hadamard32_amd as mx
+    import workloads as wl
+    mx.lib()
+    torch.cuda.set_device(0)
+    print(f"bench: generating {args.workload} inputs", file=sys.stderr, flush=True)
+    layer = Layer(mx, wl, args.workload)
+    torch.cuda.synchronize()
+    if args.copy_calibration:
+        a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        a.fill_(1.0)
+        c = torch.empty_like(a)
+        c.copy_(a)
+        torch.cuda.synchronize()
+        del a, c
+    for _ in range(args.warmup):
+        layer.step()
+    torch.cuda.synchronize()
+    print(f"bench: warmup done, timing {args.steps} steps", file=sys.stderr, flush=True)
+
+    evs = [{k: torch.cuda.Event(enable_timing=True) for k in ("q0", "q1", "w0", "w1")}
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        layer.step(evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = 1e3 * elapsed / args.steps
+    wgrad_ms = sum(e["w0"].elapsed_time(e["w1"]) for e in evs) / args.steps
+    quant_ms = sum(e["q0"].elapsed_time(e["q1"]) for e in evs) / args.steps
+
+    flops = sum(layer.flops.values())
+    value = flops / (ms_step * 1e-3) / 1e12
+    wgrad_tflops = layer.flops["wgrad"] / (wgrad_ms * 1e-3) / 1e12
+    qelems = layer.T * layer.K
+    quant_gbs = qelems * QUANT_BYTES_PER_ELEM / (quant_ms * 1e-3) / 1e9
+    traffic = load_traffic("wgrad_hbm_bytes_per_launch")
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4 (e2m1 x e2m1 with e8m0 block scales, fp32 accumulate; bf16 in/out)",
+        "data": "synthetic (seeded, generated on the GPU)",
+        "config": {"workload": args.workload, "description": layer.desc, "T": layer.T,
+                   "K": layer.K, "N": layer.N, "step": "6 quantizations + Fprop + Dgrad + Wgrad"},
+        "components": {
+            "wgrad_gemm_ms": round(wgrad_ms, 4),
+            "wgrad_gemm_tflops": round(wgrad_tflops, 2),
+            "wgrad_pct_of_fp4_peak": round(100.0 * wgrad_tflops / PEAK_FP4_TFLOPS, 2),
+            "hadamard_quant_kernel": f"mx_quantize {layer.T}x{layer.K} bf16 along rows",
+            "hadamard_quant_ms": round(quant_ms, 4),
+            "hadamard_quant_gbs": round(quant_gbs, 1),
+            "hadamard_quant_pct_of_hbm_peak": round(100.0 * quant_gbs / PEAK_HBM_GBS, 2),
+        },
+        "roofline": {
+            "kernel": "gemm_mx_kernel (Wgrad launch)",
+            "bound": "mfma",
+            "achieved": round(wgrad_tflops, 2),
+            "peak": PEAK_FP4_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(wgrad_tflops / PEAK_FP4_TFLOPS, 4),
+            "traffic": traffic,
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        cb = cpu_baseline(layer, args.cpu_sample_rows)
+        cb.pop("_numpy", None)
+        out["cpu_baseline"] = cb
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
