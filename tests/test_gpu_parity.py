@@ -166,6 +166,10 @@ GEMM_CASES = [
     (288, 320, 416),     # ragged against the 256x256 tile and the 128 k-step
     (512, 256, 1024),
     (96, 544, 2080),
+    (128, 256, 640),     # 5 k-steps: one unrolled round + 1 remainder step
+    (256, 288, 896),     # 7 k-steps: remainder of 3
+    (64, 64, 4096),      # 32 k-steps
+    (544, 800, 768),     # several tiles in both directions, partial edge tiles
 ]
 
 
