@@ -161,63 +161,125 @@ __device__ __forceinline__ void fwht_columns(float (&p)[8][8], uint32_t sign_mas
 }
 
 // ---------------------------------------------------------------------------------------------
+// Workgroup tiles of 256 rows x 128 columns for the column-blocked and 32x32 outputs. The 8 row
+// tiles that share one 64-byte segment of a transposed scale row are given to the same XCD
+// (workgroup id modulo 8) at consecutive positions, so their partial scale writes meet in one
+// L2 instead of reaching memory as partial lines. Returns false for padding workgroups.
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ bool col_tile_of(int64_t n_rt, int64_t n_ct, int64_t& rt, int64_t& ct) {
+  const int64_t bid = blockIdx.x;
+  const int64_t xcd = bid & 7, slot = bid >> 3;
+  const int64_t n_rg = (n_rt + 7) >> 3;           // groups of 8 row tiles
+  const int64_t unit = (slot >> 3) * 8 + xcd;     // (column tile, row group) pair
+  ct = unit / n_rg;
+  rt = (unit - ct * n_rg) * 8 + (slot & 7);
+  return ct < n_ct && rt < n_rt;
+}
+
+constexpr int kColTileRows = 256, kColTileCols = 128;
+constexpr int kColHalves = kColTileCols / 128;
+constexpr int kCodeStride = 144;  // LDS bytes per column of the code tile (128 + 16 padding)
+
+// ---------------------------------------------------------------------------------------------
 // 1x32 blocks down the columns (blocks along rows), output in the layout of the transpose:
-// codes_t [cols][rows/2], scales_t [cols][rows/32]. Wave w of block (bx, by) handles row block
-// rb = 4 * by + w and columns 128 * bx .. + 127; lane = 4 * column-group + q.
+// codes_t [cols][rows/2], scales_t [cols][rows/32]. A workgroup owns 256 rows x 128 columns;
+// wave w handles row blocks w and w + 4 of the tile, lane = 4 * column-group + q. Each lane's
+// 8 codes of a column (one dword) go to an LDS tile first, so the global writes are whole
+// 128-byte column pieces.
 // ---------------------------------------------------------------------------------------------
 template <bool BF16, bool HAD, bool SR, bool CEIL>
 __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
     const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, uint32_t sign_mask,
-    uint64_t seed, uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t) {
-  const int lane = threadIdx.x & 63;
-  const int q = lane & 3;
-  const int64_t rb = (int64_t)blockIdx.y * 4 + (threadIdx.x >> 6);
-  const int64_t c0 = (int64_t)blockIdx.x * 128 + (lane >> 2) * 8;
-  if (rb >= rows / 32 || c0 >= cols) return;  // whole quads leave together
-  const int64_t r0 = rb * 32 + 8 * q;
+    uint64_t seed, uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t, int64_t n_rt,
+    int64_t n_ct) {
+  __shared__ __attribute__((aligned(16))) uint8_t ctile[kColTileCols * kCodeStride];
+  __shared__ __attribute__((aligned(16))) uint8_t stile[kColTileCols * 8];
+  int64_t rt, ct;
+  if (!col_tile_of(n_rt, n_ct, rt, ct)) return;  // uniform per workgroup
 
-  float p[8][8];
-  load_patch<BF16>(x, ld, r0, c0, p);
-  if (HAD) fwht_columns(p, sign_mask, q);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int q = lane & 3, cg = lane >> 2;
+  const int64_t rb0 = rt * 8;
+  const int nrb = (int)min((int64_t)8, rows / 32 - rb0);
+  const int64_t ctile0 = ct * kColTileCols;
 
-  uint32_t sb[8];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    uint32_t m = 0;
+  for (int pass = 0; pass < 2 * kColHalves; ++pass) {
+    const int rbl = (pass & 1) * 4 + wave;
+    const int ch = pass >> 1;                 // which 128-column slice of the tile
+    const int64_t c0 = ctile0 + ch * 128 + cg * 8;
+    if (rbl >= nrb || c0 >= cols) continue;  // whole quads leave together
+    const int64_t rb = rb0 + rbl;
+    const int64_t r0 = rb * 32 + 8 * q;
+    float p[8][8];
+    load_patch<BF16>(x, ld, r0, c0, p);
+    if (HAD) fwht_columns(p, sign_mask, q);
+
+    uint32_t sb[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) m = max(m, abs_bits(p[j][k]));
-    m = max(m, dpp_u32<kQuadXor1>(m));
-    m = max(m, dpp_u32<kQuadXor2>(m));
-    sb[k] = scale_byte<CEIL>(m);
+    for (int k = 0; k < 8; ++k) {
+      uint32_t m = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m = max(m, abs_bits(p[j][k]));
+      m = max(m, dpp_u32<kQuadXor1>(m));
+      m = max(m, dpp_u32<kQuadXor2>(m));
+      sb[k] = scale_byte<CEIL>(m);
+    }
+    uint32_t r[8][8];
+    if (SR) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sr_fields8((uint64_t)((r0 + j) * cols + c0) >> 3, seed, r[j]);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      uint32_t word = 0;
+      if (sb[k] != 0xFFu) {
+        const float inv = inv_scale_from_byte(sb[k]);
+        float col[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) col[j] = p[j][k] * inv;
+        if (SR) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) word |= e2m1_sr_code(col[j], r[j][k]) << (4 * j);
+        } else {
+          word = cvt_rne_pack8(col);
+        }
+      }
+      const int cl = ch * 128 + cg * 8 + k;  // column within the tile
+      *reinterpret_cast<uint32_t*>(ctile + cl * kCodeStride + rbl * 16 + 4 * q) = word;
+      if (q == 0) stile[cl * 8 + rbl] = (uint8_t)sb[k];
+    }
   }
-  uint32_t r[8][8];
-  if (SR) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) sr_fields8((uint64_t)((r0 + j) * cols + c0) >> 3, seed, r[j]);
-  }
+  __syncthreads();
+
+  // codes: thread t writes half (t & 1) of column t >> 1 (+128 per round): row blocks
+  // 4 h .. 4 h + 3, 16 B each
   const int64_t rows2 = rows / 2;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    uint32_t word = 0;
-    if (sb[k] != 0xFFu) {
-      const float inv = inv_scale_from_byte(sb[k]);
-      float col[8];
+  for (int round = 0; round < kColHalves; ++round) {
+    const int c = round * 128 + (threadIdx.x >> 1), h = threadIdx.x & 1;
+    if (ctile0 + c < cols) {
+      uint8_t* dst = codes_t + (ctile0 + c) * rows2 + rb0 * 16;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) col[j] = p[j][k] * inv;
-      if (SR) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) word |= e2m1_sr_code(col[j], r[j][k]) << (4 * j);
-      } else {
-        word = cvt_rne_pack8(col);
+      for (int i = 0; i < 4; ++i) {
+        const int rbl = 4 * h + i;
+        if (rbl < nrb)
+          __builtin_nontemporal_store(
+              *reinterpret_cast<const u32x4*>(ctile + c * kCodeStride + rbl * 16),
+              reinterpret_cast<u32x4*>(dst + rbl * 16));
       }
     }
-    uint32_t* dst = reinterpret_cast<uint32_t*>(codes_t + (c0 + k) * rows2 + rb * 16 + 4 * q);
-    __builtin_nontemporal_store(word, dst);
   }
-  if (q == 0) {
-    const int64_t nb = rows / 32;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) scales_t[(c0 + k) * nb + rb] = (uint8_t)sb[k];
+  // scales: thread t writes the nrb scale bytes of column t (+256 per round)
+  for (int cs = threadIdx.x; cs < kColTileCols; cs += kThreads) {
+    if (ctile0 + cs >= cols) break;
+    uint8_t* dst = scales_t + (ctile0 + cs) * (rows / 32) + rb0;
+    const uint8_t* src = stile + cs * 8;
+    if (nrb == 8 && ((reinterpret_cast<uintptr_t>(dst) & 7) == 0)) {
+      *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(src);
+    } else {
+      for (int i = 0; i < nrb; ++i) dst[i] = src[i];
+    }
   }
 }
 
@@ -355,13 +417,22 @@ hipError_t launch_rows(const QuantArgs& a) {
   return hipGetLastError();
 }
 
+// Grid of the 256x128 column tiles: 64 workgroup ids per 8 (column tile, row group) units.
+inline int64_t col_tile_grid(int64_t rows, int64_t cols, int64_t& n_rt, int64_t& n_ct) {
+  n_rt = (rows + kColTileRows - 1) / kColTileRows;
+  n_ct = (cols + kColTileCols - 1) / kColTileCols;
+  const int64_t units = n_ct * ((n_rt + 7) / 8);
+  return ((units + 7) / 8) * 64;
+}
+
 template <bool BF16, bool HAD, bool SR, bool CEIL>
 hipError_t launch_cols(const QuantArgs& a) {
-  const dim3 grid((unsigned)((a.cols + 127) / 128), (unsigned)((a.rows / 32 + 3) / 4));
-  if (grid.y > 65535u) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((quant_cols_kernel<BF16, HAD, SR, CEIL>), grid, dim3(kThreads), 0,
-                     (hipStream_t)a.stream, a.x, a.rows, a.cols, a.ld, a.sign_mask, a.seed,
-                     a.codes, a.scales);
+  int64_t n_rt, n_ct;
+  const int64_t nblocks = col_tile_grid(a.rows, a.cols, n_rt, n_ct);
+  if (nblocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((quant_cols_kernel<BF16, HAD, SR, CEIL>), dim3((unsigned)nblocks),
+                     dim3(kThreads), 0, (hipStream_t)a.stream, a.x, a.rows, a.cols, a.ld,
+                     a.sign_mask, a.seed, a.codes, a.scales, n_rt, n_ct);
   return hipGetLastError();
 }
 
