@@ -245,7 +245,7 @@ def main():
             "hadamard_quant_pct_of_hbm_peak": round(100.0 * quant_gbs / PEAK_HBM_GBS, 2),
         },
         "roofline": {
-            "kernel": "gemm_mx_kernel (Wgrad launch)",
+            "kernel": "gemm_mx_stream_kernel (Wgrad launch)",
             "bound": "mfma",
             "achieved": round(wgrad_tflops, 2),
             "peak": PEAK_FP4_TFLOPS,

@@ -42,6 +42,7 @@ constexpr int kRowBytes = kBK / 2;       // 64 bytes of codes per row per step
 constexpr int kThreads = 256;
 constexpr int kTileBytes = kBM * kRowBytes;           // 16 KiB per operand per stage
 constexpr int kStageBytes = 2 * kTileBytes + 2 * kBM * 4;
+constexpr int kStreamWaves = 4;  // waves per workgroup of the streaming kernel (4 or 8)
 
 __device__ __forceinline__ int swz(int row, int chunk) {
   return row * kRowBytes + ((chunk ^ ((row >> 2) & 3)) << 4);
@@ -69,6 +70,14 @@ struct StepRegs {
 struct Frags {
   u32x4 a[4], b[4];  // 16 bytes = 32 FP4 values per lane (the MFMA reads 4 registers for FP4)
 };
+
+template <int N, typename F, int I = 0>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, F, I + 1>(static_cast<F&&>(f));
+  }
+}
 
 __device__ __forceinline__ v8i as_operand(const u32x4& v) {
   return v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
@@ -308,15 +317,56 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// Streaming kernel, templated on the k-extent of one LDS stage. BKS = number of 64-wide k
+// sub-steps per stage: 2 (128 k = 64 bytes per row) with 4 stages, or 4 (256 k = 128 bytes per
+// row) with 2 stages. With 128-byte rows every direct load instruction covers whole 128-byte
+// lines (8 rows x 128 B), which quarters the number of L1->L2 requests per byte compared with
+// 64-byte row pieces; the L2 request rate, not its bandwidth, is what bounds this kernel.
+// WAVES = 4: one wave per SIMD, each wave owns 128x128 (4x4 MFMA tiles, 256 accumulators).
+// WAVES = 8: two waves per SIMD, each wave owns 64x128 (2x4 MFMA tiles).
+template <int WAVES, int BKS, int STAGES>
+struct StreamCfg {
+  static constexpr int kRow = 32 * BKS;                         // code bytes per row per stage
+  static constexpr int kTile = kBM * kRow;                      // per operand
+  static constexpr int kScaleRow = 2 * BKS;                     // scale bytes per row per stage
+  // BKS == 4: scales do not travel with the stage. A separate double-buffered area holds 4
+  // steps (32 bytes) of scales per row, fetched as 32-byte pieces (one L2 request per row per
+  // 4 steps instead of one per step); each step brings in one quarter of the next group.
+  static constexpr bool kGroupScales = BKS == 4;
+  static constexpr int kGroupSteps = 4;
+  static constexpr int kGroupRow = kGroupSteps * kScaleRow;     // 32 bytes
+  static constexpr int kGroupBytes = 2 * kBM * kGroupRow;       // both operands, 16 KiB
+  static constexpr int kStage = 2 * kTile + (kGroupScales ? 0 : 2 * kBM * kScaleRow);
+  static constexpr int kLds = STAGES * kStage + (kGroupScales ? 2 * kGroupBytes : 0);
+  static constexpr int kRowsPerBlock = 1024 / kRow;             // rows per 1 KiB code load
+  static constexpr int kCodeLoads = kBM / kRowsPerBlock / WAVES;  // per operand per wave
+  static constexpr int kScaleLoads = kGroupScales ? kGroupBytes / 1024 / kGroupSteps / WAVES
+                                                  : 2 * (kBM * kScaleRow / 256) / WAVES;
+  static constexpr int kLoads = 2 * kCodeLoads + kScaleLoads;
+  static constexpr int kSwzShift = BKS == 2 ? 2 : 1;            // rows sharing a bank phase
+  // byte offset of 16-byte chunk `chunk` of row `row` in a stage's code tile: the chunk
+  // position is XOR-ed with a row phase so that 16 consecutive rows hit distinct bank groups
+  __device__ static __forceinline__ int swz(int row, int chunk) {
+    return row * kRow + ((chunk ^ ((row >> kSwzShift) & (2 * BKS - 1))) << 4);
+  }
+};
+
+template <int WAVES, int BKS, int STAGES>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(WAVES / 4, WAVES / 4)))
 void gemm_mx_stream_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, int lga,
                            const uint8_t* __restrict__ B, const uint8_t* __restrict__ Bs, int lgb,
                            int64_t M, int64_t N, int64_t K, float alpha_f, int out_bf16,
                            void* __restrict__ C, int64_t ldc, int nbm, int nbn) {
-  __shared__ __attribute__((aligned(1024))) uint8_t st0[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t st1[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t st2[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t st3[kStageBytes];
+  using Cfg = StreamCfg<WAVES, BKS, STAGES>;
+  static_assert(WAVES == 4 || WAVES == 8, "4 or 8 waves");
+  static_assert((BKS == 2 && STAGES == 4) || (BKS == 4 && STAGES == 2), "stage shapes");
+  constexpr int FA = WAVES == 4 ? 4 : 2;   // 32-row A fragments per wave
+  constexpr int FB = 4;                    // 32-row B fragments per wave
+  constexpr int WM = kBM / (32 * FA);      // waves along M
+  constexpr int SW = BKS / 2;              // scale words per row per stage
+  constexpr int LOADS = Cfg::kLoads;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg::kLds];
+  uint8_t* const sgroup = smem + STAGES * Cfg::kStage;  // scale groups (BKS == 4)
 
   const int nblocks = nbm * nbn;
   int bid = blockIdx.x;
@@ -333,9 +383,9 @@ void gemm_mx_stream_kernel(const uint8_t* __restrict__ A, const uint8_t* __restr
 
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % WM, wn = wave / WM;
   const int64_t kbytes = K / 2, nkb = K / 32;
-  const int nk = (int)(K / kBK);
+  const int nk = (int)(K / (64 * BKS));
   const int frow = lane & 31, fhalf = lane >> 5;
 
   const int64_t rows_a = min((int64_t)kBM, M - m0), rows_b = min((int64_t)kBN, N - n0);
@@ -346,126 +396,233 @@ void gemm_mx_stream_kernel(const uint8_t* __restrict__ A, const uint8_t* __restr
   const int64_t sbytes_b = (((n0 + rows_b - 1) >> lgb) - s0b + 1) * nkb;
   const i32x4 rsa = rsrc_words(As + s0a * nkb, sbytes_a);
   const i32x4 rsb = rsrc_words(Bs + s0b * nkb, sbytes_b);
-  // code slot of this lane in load i: row 16 (4 i + wave) + lane / 4, k-chunk as in swz()
-  const int crow = 16 * wave + (lane >> 2);
-  const int cchunk = (lane & 3) ^ ((lane >> 4) & 3);
-  const int voff = (int)(crow * kbytes) + 16 * cchunk;  // + i * 64 rows for load i
-  const int row_step = (int)(64 * kbytes);
-  // scale word of row 64 wave + lane
-  const int srow = 64 * wave + lane;
-  const int soff_a = srow < rows_a ? (int)((((m0 + srow) >> lga) - s0a) * nkb) : (int)sbytes_a;
-  const int soff_b = srow < rows_b ? (int)((((n0 + srow) >> lgb) - s0b) * nkb) : (int)sbytes_b;
 
+  // code load i of this wave fills 1 KiB block b = i * WAVES + wave of the tile: rows
+  // kRowsPerBlock * b + lane / (2 BKS), position lane % (2 BKS), i.e. chunk position ^ phase
+  int voff[Cfg::kCodeLoads];
+#pragma unroll
+  for (int i = 0; i < Cfg::kCodeLoads; ++i) {
+    const int b = i * WAVES + wave;
+    const int row = Cfg::kRowsPerBlock * b + lane / (2 * BKS);
+    const int pos = lane % (2 * BKS);
+    const int chunk = pos ^ ((row >> Cfg::kSwzShift) & (2 * BKS - 1));
+    voff[i] = (int)(row * kbytes) + 16 * chunk;
+  }
+  // scale load j of this wave: 256-byte piece q of operand o (rows of 2 BKS bytes, lane ->
+  // row piece * (128 / BKS) + lane / SW, word lane % SW); rows past the operand read zero
+  constexpr int kPieces = kBM * Cfg::kScaleRow / 256;  // per operand
+  int soff[Cfg::kGroupScales ? 1 : Cfg::kScaleLoads];
+  if constexpr (!Cfg::kGroupScales) {
+    if constexpr (!Cfg::kGroupScales)
+#pragma unroll
+    for (int j = 0; j < Cfg::kScaleLoads; ++j) {
+      const int sidx = wave + j * WAVES;
+      const int o = sidx / kPieces, q = sidx % kPieces;
+      const int row = q * (128 / BKS) + lane / SW;
+      const int word = lane % SW;
+      if (o == 0)
+        soff[j] = row < rows_a ? (int)((((m0 + row) >> lga) - s0a) * nkb) + 4 * word : (int)sbytes_a;
+      else
+        soff[j] = row < rows_b ? (int)((((n0 + row) >> lgb) - s0b) * nkb) + 4 * word : (int)sbytes_b;
+    }
+  }
+  // group mode: quarter p of a group holds rows 128 p .. 128 p + 127 of the 512 scale rows
+  // (A rows 0-255, then B); wave w loads rows 128 p + 32 w + lane / 2, 16-byte half lane % 2.
+  // Quarters 0-1 are A rows, 2-3 are B rows, so the operand depends on p only.
+  int goff[4];
+  if constexpr (Cfg::kGroupScales) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int row = (128 * p + 32 * wave + (lane >> 1)) & (kBM - 1);
+      const int half = lane & 1;
+      if (p < 2)
+        goff[p] = row < rows_a ? (int)((((m0 + row) >> lga) - s0a) * nkb) + 16 * half : (int)sbytes_a;
+      else
+        goff[p] = row < rows_b ? (int)((((n0 + row) >> lgb) - s0b) * nkb) + 16 * half : (int)sbytes_b;
+    }
+  }
+  const int ngroups = (nk + Cfg::kGroupSteps - 1) / Cfg::kGroupSteps;
+  // quarter p of scale group g into buffer g % 2 (groups past the end re-read the last one)
+  auto issue_group_part = [&](int g, int p) {
+    const int gs = min(g, ngroups - 1);
+    const uint32_t dst = lds_addr(sgroup + (g & 1) * Cfg::kGroupBytes + (128 * p + 32 * wave) * Cfg::kGroupRow);
+    const i32x4 sel = p < 2 ? rsa : rsb;
+    dma_b128(sel, dst, goff[p], gs * Cfg::kGroupRow);
+  };
+
+  auto stage_ptr = [&](int st) { return smem + st * Cfg::kStage; };
   auto issue = [&](uint8_t* st, int ks) {
-    const int kofs = ks * kRowBytes;
-    const uint32_t base = lds_addr(st + 1024 * wave);
+    const int kofs = ks * Cfg::kRow;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      dma_b128(ra, base + 4096 * i, voff + i * row_step, kofs);
-      dma_b128(rb, base + 4096 * i + kTileBytes, voff + i * row_step, kofs);
+    for (int i = 0; i < Cfg::kCodeLoads; ++i) {
+      const uint32_t dst = lds_addr(st + 1024 * (i * WAVES + wave));
+      dma_b128(ra, dst, voff[i], kofs);
+      dma_b128(rb, dst + Cfg::kTile, voff[i], kofs);
     }
-    const uint32_t sbase = lds_addr(st + 2 * kTileBytes + 256 * wave);
-    dma_b32(rsa, sbase, soff_a, 4 * ks);
-    dma_b32(rsb, sbase + kBM * 4, soff_b, 4 * ks);
+    if constexpr (!Cfg::kGroupScales)
+#pragma unroll
+    for (int j = 0; j < Cfg::kScaleLoads; ++j) {
+      const int sidx = wave + j * WAVES;
+      const int o = sidx / kPieces, q = sidx % kPieces;
+      const uint32_t dst = lds_addr(st + 2 * Cfg::kTile + o * kBM * Cfg::kScaleRow + 256 * q);
+      const i32x4 sel = o == 0 ? rsa : rsb;  // wave-uniform; pin it to scalar registers
+      const i32x4 rs = {__builtin_amdgcn_readfirstlane(sel.x), __builtin_amdgcn_readfirstlane(sel.y),
+                        __builtin_amdgcn_readfirstlane(sel.z), __builtin_amdgcn_readfirstlane(sel.w)};
+      dma_b32(rs, dst, soff[j], ks * Cfg::kScaleRow);
+    }
   };
-  auto lread = [&](const uint8_t* st, int ki, Frags& f) {
+  auto lread = [&](const uint8_t* st, int sub, u32x4 (&fa)[FA], u32x4 (&fb)[FB]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f.a[i] = *reinterpret_cast<const u32x4*>(st + swz(wm * 128 + 32 * i + frow, 2 * ki + fhalf));
-      f.b[i] = *reinterpret_cast<const u32x4*>(st + kTileBytes +
-                                               swz(wn * 128 + 32 * i + frow, 2 * ki + fhalf));
-    }
+    for (int i = 0; i < FA; ++i)
+      fa[i] = *reinterpret_cast<const u32x4*>(st + Cfg::swz(wm * 32 * FA + 32 * i + frow, 2 * sub + fhalf));
+#pragma unroll
+    for (int j = 0; j < FB; ++j)
+      fb[j] = *reinterpret_cast<const u32x4*>(st + Cfg::kTile +
+                                              Cfg::swz(wn * 32 * FB + 32 * j + frow, 2 * sub + fhalf));
   };
-  auto sread = [&](const uint8_t* st, uint32_t (&sa)[4], uint32_t (&sb)[4]) {
-    const uint32_t* pa = reinterpret_cast<const uint32_t*>(st + 2 * kTileBytes);
-    const uint32_t* pb = reinterpret_cast<const uint32_t*>(st + 2 * kTileBytes + kBM * 4);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sa[i] = pa[wm * 128 + 32 * i + frow] >> (8 * fhalf);
-      sb[i] = pb[wn * 128 + 32 * i + frow] >> (8 * fhalf);
+  // per-lane scale words of a stage: word w holds k-blocks 4w..4w+3 of the row; lanes 0-31
+  // use the even blocks, lanes 32-63 the odd ones, so shift by one byte on the upper half and
+  // let op_sel 0 / 2 pick sub-step 2w / 2w+1
+  auto sread = [&](const uint8_t* st, int ks, uint32_t (&sa)[FA][SW], uint32_t (&sb)[FB][SW]) {
+    const uint32_t* pa;
+    const uint32_t* pb;
+    int stride;  // words per row
+    if constexpr (Cfg::kGroupScales) {
+      const uint8_t* gb = sgroup + ((ks / Cfg::kGroupSteps) & 1) * Cfg::kGroupBytes +
+                          (ks % Cfg::kGroupSteps) * Cfg::kScaleRow;
+      pa = reinterpret_cast<const uint32_t*>(gb);
+      pb = reinterpret_cast<const uint32_t*>(gb + kBM * Cfg::kGroupRow);
+      stride = Cfg::kGroupRow / 4;
+    } else {
+      pa = reinterpret_cast<const uint32_t*>(st + 2 * Cfg::kTile);
+      pb = reinterpret_cast<const uint32_t*>(st + 2 * Cfg::kTile + kBM * Cfg::kScaleRow);
+      stride = SW;
     }
+#pragma unroll
+    for (int i = 0; i < FA; ++i)
+#pragma unroll
+      for (int w = 0; w < SW; ++w) sa[i][w] = pa[(wm * 32 * FA + 32 * i + frow) * stride + w] >> (8 * fhalf);
+#pragma unroll
+    for (int j = 0; j < FB; ++j)
+#pragma unroll
+      for (int w = 0; w < SW; ++w) sb[j][w] = pb[(wn * 32 * FB + 32 * j + frow) * stride + w] >> (8 * fhalf);
   };
 
-  v16f acc[4][4];
+  v16f acc[FA][FB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FA; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < FB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-  auto mma = [&](const Frags& f, const uint32_t (&sa)[4], const uint32_t (&sb)[4], auto opsel) {
-    constexpr int OP = decltype(opsel)::value;
+  // MFMAs of sub-step SUB: scale word SUB / 2, byte pair selected by op_sel 2 * (SUB % 2)
+  auto mma = [&](const u32x4 (&fa)[FA], const u32x4 (&fb)[FB], const uint32_t (&sa)[FA][SW],
+                 const uint32_t (&sb)[FB][SW], auto sub) {
+    constexpr int SUB = decltype(sub)::value;
+    constexpr int OP = 2 * (SUB % 2), W = SUB / 2;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < FA; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < FB; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            as_operand(f.b[j]), as_operand(f.a[i]), acc[i][j], 4, 4, OP, sb[j], OP, sa[i]);
+            as_operand(fb[j]), as_operand(fa[i]), acc[i][j], 4, 4, OP, sb[j][W], OP, sa[i][W]);
   };
-  using Op0 = std::integral_constant<int, 0>;
-  using Op2 = std::integral_constant<int, 2>;
 
-  Frags F0, F1;
-  uint32_t saC[4], sbC[4], saN[4], sbN[4];
+  u32x4 fa0[FA], fb0[FB], fa1[FA], fb1[FB];
+  uint32_t saC[FA][SW], sbC[FB][SW], saN[FA][SW], sbN[FB][SW];
 
-  // Every step issues exactly 10 loads per wave (steps past the end re-read step nk-1 into a
-  // stage nobody reads again), so the wait before each barrier is always "all but the newest
-  // 10", i.e. the step about to be read has landed, and the loop body has no branches.
+  // Every step issues exactly LOADS loads per wave (steps past the end re-read step nk-1 into
+  // a stage nobody reads again), so each wait is a constant count and the loop has no branches.
   auto issue_step = [&](uint8_t* st, int ks) { issue(st, min(ks, nk - 1)); };
+  static_assert(Cfg::kGroupScales ? Cfg::kScaleLoads == 1 : true, "one scale quarter per step");
 
-  // prologue: steps 0, 1, 2 in flight; wait for step 0 everywhere
-  issue_step(st0, 0);
-  issue_step(st1, 1);
-  issue_step(st2, 2);
-  wait_vmcnt<20>();
-  __builtin_amdgcn_s_barrier();
-  sread(st0, saC, sbC);
-  lread(st0, 0, F0);
-
-  // step ks on stage cur: read its second k-half; MFMAs of the first half; wait until step ks+1
-  // has landed (own loads; the barrier covers the other waves) and every wave has finished
-  // reading stage ks-1; refill that stage with step ks+3; read the first half and scales of
-  // ks+1; MFMAs of the second half of ks.
-  auto body = [&](int ks, const uint8_t* cur, const uint8_t* nxt, uint8_t* refill) {
-    lread(cur, 1, F1);
-    mma(F0, saC, sbC, Op0{});
-    __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<10>();
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage ks are done
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    issue_step(refill, ks + 3);
-    sread(nxt, saN, sbN);
-    lread(nxt, 0, F0);
-    mma(F1, saC, sbC, Op2{});
+  // Group mode schedule: the load bundle of step j (its code loads, issued two steps ahead)
+  // also carries quarter (j + 3) % 4 of scale group (j + 3) / 4, so group G arrives with the
+  // bundles of steps 4G-3 .. 4G. That makes it complete (loads retire in order) when the
+  // scales of step 4G are first read, at the barrier of step 4G-1, and its first quarter is
+  // requested only after the barrier of step 4G-5, after which nobody reads the previous
+  // occupant of its buffer (group G-2) any more. Quarters 0-2 of group 0 go out on their own.
+  auto issue_bundle = [&](uint8_t* st, int j) {
+    issue_step(st, j);
+    if constexpr (Cfg::kGroupScales) issue_group_part((j + 3) / 4, (j + 3) % 4);
+  };
+  if constexpr (Cfg::kGroupScales) {
+    issue_group_part(0, 0);
+    issue_group_part(0, 1);
+    issue_group_part(0, 2);
+  }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      saC[i] = saN[i];
-      sbC[i] = sbN[i];
-    }
+  for (int s = 0; s < STAGES; ++s) issue_bundle(stage_ptr(s), s);
+  wait_vmcnt<(STAGES - 1) * LOADS>();
+  __builtin_amdgcn_s_barrier();
+  sread(stage_ptr(0), 0, saC, sbC);
+  lread(stage_ptr(0), 0, fa0, fb0);
+
+  // Step ks on stage cur: sub-steps 0 .. BKS-1, fragments read one sub-step ahead (ping-pong
+  // fa0/fb0, fa1/fb1). Before the MFMAs of the last sub-step: wait until step ks+1 has landed
+  // (own loads; the barrier covers the other waves; steps ks+2 .. ks+STAGES-1 may still be in
+  // flight); every wave then holds all of stage ks in registers, so the stage is refilled at
+  // once with step ks+STAGES; the scales and first sub-step of ks+1 are read meanwhile.
+  auto body = [&](int ks, uint8_t* cur, const uint8_t* nxt) {
+    static_for<BKS>([&](auto sub) {
+      constexpr int S = decltype(sub)::value;
+      if constexpr (S + 1 < BKS) {
+        if constexpr (S % 2 == 0) lread(cur, S + 1, fa1, fb1);
+        else lread(cur, S + 1, fa0, fb0);
+      } else {
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<(STAGES - 2) * LOADS>();
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage ks are done
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        issue_bundle(cur, ks + STAGES);
+        sread(nxt, ks + 1, saN, sbN);
+        lread(nxt, 0, fa0, fb0);  // the last sub-step (odd) uses fa1/fb1
+      }
+      if constexpr (S % 2 == 0) mma(fa0, fb0, saC, sbC, sub);
+      else mma(fa1, fb1, saC, sbC, sub);
+      __builtin_amdgcn_sched_barrier(0);  // keep one sub-step of fragments live at a time
+    });
+#pragma unroll
+    for (int i = 0; i < FA; ++i)
+#pragma unroll
+      for (int w = 0; w < SW; ++w) saC[i][w] = saN[i][w];
+#pragma unroll
+    for (int j = 0; j < FB; ++j)
+#pragma unroll
+      for (int w = 0; w < SW; ++w) sbC[j][w] = sbN[j][w];
   };
   int ks = 0;
+  if constexpr (STAGES == 4) {
 #pragma unroll 1
-  for (; ks + 4 <= nk; ks += 4) {
-    body(ks, st0, st1, st3);
-    body(ks + 1, st1, st2, st0);
-    body(ks + 2, st2, st3, st1);
-    body(ks + 3, st3, st0, st2);
+    for (; ks + 4 <= nk; ks += 4) {
+      body(ks, stage_ptr(0), stage_ptr(1));
+      body(ks + 1, stage_ptr(1), stage_ptr(2));
+      body(ks + 2, stage_ptr(2), stage_ptr(3));
+      body(ks + 3, stage_ptr(3), stage_ptr(0));
+    }
+    if (ks < nk) body(ks, stage_ptr(0), stage_ptr(1));
+    if (ks + 1 < nk) body(ks + 1, stage_ptr(1), stage_ptr(2));
+    if (ks + 2 < nk) body(ks + 2, stage_ptr(2), stage_ptr(3));
+  } else {
+    // one body per iteration with computed stage pointers: unrolling two steps here doubles
+    // the live fragment registers and spills
+#pragma unroll 1
+    for (; ks < nk; ++ks) body(ks, stage_ptr(ks & 1), stage_ptr((ks + 1) & 1));
   }
-  if (ks < nk) body(ks, st0, st1, st3);
-  if (ks + 1 < nk) body(ks + 1, st1, st2, st0);
-  if (ks + 2 < nk) body(ks + 2, st2, st3, st1);
   wait_vmcnt<0>();  // no load may still be writing LDS when the workgroup ends
 
+  // epilogue: acc[i][j][r] = C[m][n], m = wm*32FA + 32 i + (lane % 32),
+  //           n = wn*128 + 32 j + 8 (r / 4) + 4 (lane / 32) + r % 4
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t m = m0 + wm * 128 + 32 * i + frow;
+  for (int i = 0; i < FA; ++i) {
+    const int64_t m = m0 + wm * 32 * FA + 32 * i + frow;
     if (m >= M) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < FB; ++j) {
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
-        const int64_t n = n0 + wn * 128 + 32 * j + 8 * rq + 4 * fhalf;
+        const int64_t n = n0 + wn * 32 * FB + 32 * j + 8 * rq + 4 * fhalf;
         if (n >= N) continue;
         const float v0 = acc[i][j][4 * rq + 0] * alpha_f;
         const float v1 = acc[i][j][4 * rq + 1] * alpha_f;
@@ -495,8 +652,14 @@ hipError_t mx_launch_gemm(const GemmArgs& g) {
   const float alpha_f = __builtin_bit_cast(float, (uint32_t)(g.alpha + 127) << 23);
   const int lga = g.ga == 32 ? 5 : 0, lgb = g.gb == 32 ? 5 : 0;
   const dim3 grid((unsigned)(nbm * nbn));
-  if (g.K % kBK == 0 && g.K > 0)
-    hipLaunchKernelGGL(gemm_mx_stream_kernel, grid, dim3(kThreads), 0, (hipStream_t)g.stream, g.a,
+  if (g.K % 512 == 0 && g.K > 0)
+    hipLaunchKernelGGL((gemm_mx_stream_kernel<kStreamWaves, 4, 2>), grid, dim3(64 * kStreamWaves), 0,
+                       (hipStream_t)g.stream, g.a,
+                       g.as, lga, g.b, g.bs, lgb, g.M, g.N, g.K, alpha_f, g.out_bf16 ? 1 : 0, g.c,
+                       g.ldc, (int)nbm, (int)nbn);
+  else if (g.K % kBK == 0 && g.K > 0)
+    hipLaunchKernelGGL((gemm_mx_stream_kernel<kStreamWaves, 2, 4>), grid, dim3(64 * kStreamWaves), 0,
+                       (hipStream_t)g.stream, g.a,
                        g.as, lga, g.b, g.bs, lgb, g.M, g.N, g.K, alpha_f, g.out_bf16 ? 1 : 0, g.c,
                        g.ldc, (int)nbm, (int)nbn);
   else

@@ -170,6 +170,8 @@ GEMM_CASES = [
     (256, 288, 896),     # 7 k-steps: remainder of 3
     (64, 64, 4096),      # 32 k-steps
     (544, 800, 768),     # several tiles in both directions, partial edge tiles
+    (256, 256, 2560),    # 256-wide k stages: 10 steps, last scale group partial
+    (288, 96, 1536),     # 6 steps, partial M tile
 ]
 
 
@@ -187,9 +189,10 @@ def test_gemm_within_bound(mx, orc, M, N, K, out_dtype, which):
     check_gemm(out, C, Cabs)
 
 
+@pytest.mark.parametrize("K", [384, 2048])
 @pytest.mark.parametrize("ga,gb", [(32, 1), (1, 32), (32, 32)])
-def test_gemm_2d_scales(mx, orc, ga, gb):
-    M, N, K = 288, 256, 384
+def test_gemm_2d_scales(mx, orc, ga, gb, K):
+    M, N = 288, 256
     a = wl.student_t3((M, K), seed=1).to(DEV)
     b = wl.student_t3((N, K), seed=2).to(DEV)
     aq, as_ = (mx.mx_quantize_2d(a, scale_rule=1)[:2] if ga == 32 else mx.mx_quantize(a, scale_rule=1))
