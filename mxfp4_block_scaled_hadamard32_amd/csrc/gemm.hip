@@ -35,6 +35,9 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBM = 256, kBN = 256;
 constexpr int kBK = 128;                 // k elements per step
@@ -340,7 +343,11 @@ struct StreamCfg {
   static constexpr int kLds = STAGES * kStage + (kGroupScales ? 2 * kGroupBytes : 0);
   static constexpr int kRowsPerBlock = 1024 / kRow;             // rows per 1 KiB code load
   static constexpr int kCodeLoads = kBM / kRowsPerBlock / WAVES;  // per operand per wave
-  static constexpr int kScaleLoads = kGroupScales ? kGroupBytes / 1024 / kGroupSteps / WAVES
+  // a group quarter (128 rows x 32 bytes) is split evenly over the waves: one 16-byte load
+  // per lane with 4 waves, two 4-byte loads per lane with 8 (there is no 8-byte direct load)
+  static constexpr int kGroupLaneBytes = WAVES == 4 ? 16 : 4;
+  static constexpr int kGroupLoads = kGroupBytes / 4 / WAVES / (64 * kGroupLaneBytes);
+  static constexpr int kScaleLoads = kGroupScales ? kGroupLoads
                                                   : 2 * (kBM * kScaleRow / 256) / WAVES;
   static constexpr int kLoads = 2 * kCodeLoads + kScaleLoads;
   static constexpr int kSwzShift = BKS == 2 ? 2 : 1;            // rows sharing a bank phase
@@ -351,7 +358,7 @@ struct StreamCfg {
   }
 };
 
-template <int WAVES, int BKS, int STAGES>
+template <int WAVES, int BKS, int STAGES, int SPLIT3 = 0, int SPLIT0 = 0, int SPLIT1 = 0>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(WAVES / 4, WAVES / 4)))
 void gemm_mx_stream_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, int lga,
                            const uint8_t* __restrict__ B, const uint8_t* __restrict__ Bs, int lgb,
@@ -427,27 +434,40 @@ void gemm_mx_stream_kernel(const uint8_t* __restrict__ A, const uint8_t* __restr
     }
   }
   // group mode: quarter p of a group holds rows 128 p .. 128 p + 127 of the 512 scale rows
-  // (A rows 0-255, then B); wave w loads rows 128 p + 32 w + lane / 2, 16-byte half lane % 2.
-  // Quarters 0-1 are A rows, 2-3 are B rows, so the operand depends on p only.
-  int goff[4];
+  // (A rows 0-255, then B), 32 bytes each. Load h of wave w covers bytes
+  // (w G + h) 64 LB .. +64 LB of the quarter (G loads per wave, LB bytes per lane), so lane l
+  // fetches byte (q % 32) of row 128 p + q / 32 for q = ((w G + h) 64 + l) LB. Quarters 0-1 are
+  // A rows, 2-3 are B rows, so the operand depends on p only.
+  constexpr int kGL = Cfg::kGroupLoads, kLB = Cfg::kGroupLaneBytes;
+  int goff[4][Cfg::kGroupScales ? kGL : 1];
   if constexpr (Cfg::kGroupScales) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int row = (128 * p + 32 * wave + (lane >> 1)) & (kBM - 1);
-      const int half = lane & 1;
-      if (p < 2)
-        goff[p] = row < rows_a ? (int)((((m0 + row) >> lga) - s0a) * nkb) + 16 * half : (int)sbytes_a;
-      else
-        goff[p] = row < rows_b ? (int)((((n0 + row) >> lgb) - s0b) * nkb) + 16 * half : (int)sbytes_b;
-    }
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+      for (int h = 0; h < kGL; ++h) {
+        const int q = ((wave * kGL + h) * 64 + lane) * kLB;
+        const int row = (128 * p + q / Cfg::kGroupRow) & (kBM - 1);
+        const int byte = q % Cfg::kGroupRow;
+        if (p < 2)
+          goff[p][h] = row < rows_a ? (int)((((m0 + row) >> lga) - s0a) * nkb) + byte : (int)sbytes_a;
+        else
+          goff[p][h] = row < rows_b ? (int)((((n0 + row) >> lgb) - s0b) * nkb) + byte : (int)sbytes_b;
+      }
   }
   const int ngroups = (nk + Cfg::kGroupSteps - 1) / Cfg::kGroupSteps;
-  // quarter p of scale group g into buffer g % 2 (groups past the end re-read the last one)
-  auto issue_group_part = [&](int g, int p) {
+  // load h of quarter p of scale group g into buffer g % 2 (groups past the end re-read the
+  // last one)
+  auto issue_group_load = [&](int g, int p, int h) {
     const int gs = min(g, ngroups - 1);
-    const uint32_t dst = lds_addr(sgroup + (g & 1) * Cfg::kGroupBytes + (128 * p + 32 * wave) * Cfg::kGroupRow);
+    const uint32_t dst = lds_addr(sgroup + (g & 1) * Cfg::kGroupBytes + 128 * p * Cfg::kGroupRow +
+                                  (wave * kGL + h) * 64 * kLB);
     const i32x4 sel = p < 2 ? rsa : rsb;
-    dma_b128(sel, dst, goff[p], gs * Cfg::kGroupRow);
+    if constexpr (kLB == 16) dma_b128(sel, dst, goff[p][h], gs * Cfg::kGroupRow);
+    else dma_b32(sel, dst, goff[p][h], gs * Cfg::kGroupRow);
+  };
+  auto issue_group_part = [&](int g, int p) {
+#pragma unroll
+    for (int h = 0; h < kGL; ++h) issue_group_load(g, p, h);
   };
 
   auto stage_ptr = [&](int st) { return smem + st * Cfg::kStage; };
@@ -534,7 +554,6 @@ void gemm_mx_stream_kernel(const uint8_t* __restrict__ A, const uint8_t* __restr
   // Every step issues exactly LOADS loads per wave (steps past the end re-read step nk-1 into
   // a stage nobody reads again), so each wait is a constant count and the loop has no branches.
   auto issue_step = [&](uint8_t* st, int ks) { issue(st, min(ks, nk - 1)); };
-  static_assert(Cfg::kGroupScales ? Cfg::kScaleLoads == 1 : true, "one scale quarter per step");
 
   // Group mode schedule: the load bundle of step j (its code loads, issued two steps ahead)
   // also carries quarter (j + 3) % 4 of scale group (j + 3) / 4, so group G arrives with the
@@ -546,14 +565,57 @@ void gemm_mx_stream_kernel(const uint8_t* __restrict__ A, const uint8_t* __restr
     issue_step(st, j);
     if constexpr (Cfg::kGroupScales) issue_group_part((j + 3) / 4, (j + 3) % 4);
   };
+  // Spread schedule (2 stages): load L of bundle j (L < S: load L of its scale quarter, S the
+  // number of scale loads per step; L = S + q: code load q / 2 of operand q % 2) is issued
+  // between MFMAs instead of in one burst after the
+  // barrier, so that a full address queue stalls a single load rather than the whole sub-step.
+  // Loads 0 .. kP3-1 go out during the last sub-step of step j-2 (right after its barrier),
+  // the rest during sub-steps 0 .. 2 of step j-1; all of them land by the barrier of step j-1.
+  constexpr int kP3 = SPLIT3, kP0 = SPLIT0, kP1 = SPLIT1, kP2 = LOADS - kP3 - kP0 - kP1;
+  static_assert(STAGES != 2 || (kP2 >= 0 && 2 * kP3 <= FA * FB && 2 * kP0 <= FA * FB && 2 * kP1 <= FA * FB &&
+                2 * kP2 <= FA * FB), "at most one load per MFMA pair");
+  auto issue_load = [&](uint8_t* st, int j, int L) {
+    if (L < Cfg::kScaleLoads) {
+      issue_group_load((j + 3) / 4, (j + 3) % 4, L);
+    } else {
+      const int q = L - Cfg::kScaleLoads, i = q >> 1;
+      const uint32_t dst = lds_addr(st + 1024 * (i * WAVES + wave)) + ((q & 1) ? Cfg::kTile : 0);
+      dma_b128((q & 1) ? rb : ra, dst, voff[i], min(j, nk - 1) * Cfg::kRow);
+    }
+  };
+  // the same MFMAs with loads FIRST .. FIRST+CNT-1 of bundle j (into stage st) issued after
+  // every second MFMA
+  auto mma_mix = [&](const u32x4 (&fa)[FA], const u32x4 (&fb)[FB], const uint32_t (&sa)[FA][SW],
+                     const uint32_t (&sb)[FB][SW], auto sub, uint8_t* st, int j, auto first,
+                     auto count) {
+    constexpr int SUB = decltype(sub)::value;
+    constexpr int OP = 2 * (SUB % 2), W = SUB / 2;
+    constexpr int FIRST = decltype(first)::value, CNT = decltype(count)::value;
+    static_for<FA * FB>([&](auto nn) {
+      constexpr int n = decltype(nn)::value, i = n / FB, jj = n % FB;
+      acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          as_operand(fb[jj]), as_operand(fa[i]), acc[i][jj], 4, 4, OP, sb[jj][W], OP, sa[i][W]);
+      if constexpr (n % 2 == 1 && n / 2 < CNT) {
+        issue_load(st, j, FIRST + n / 2);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    });
+  };
+
   if constexpr (Cfg::kGroupScales) {
     issue_group_part(0, 0);
     issue_group_part(0, 1);
     issue_group_part(0, 2);
   }
+  if constexpr (STAGES == 2) {
+    static_for<LOADS>([&](auto L) { issue_load(stage_ptr(0), 0, decltype(L)::value); });
+    static_for<kP3>([&](auto L) { issue_load(stage_ptr(1), 1, decltype(L)::value); });
+    wait_vmcnt<kP3>();
+  } else {
 #pragma unroll
-  for (int s = 0; s < STAGES; ++s) issue_bundle(stage_ptr(s), s);
-  wait_vmcnt<(STAGES - 1) * LOADS>();
+    for (int s = 0; s < STAGES; ++s) issue_bundle(stage_ptr(s), s);
+    wait_vmcnt<(STAGES - 1) * LOADS>();
+  }
   __builtin_amdgcn_s_barrier();
   sread(stage_ptr(0), 0, saC, sbC);
   lread(stage_ptr(0), 0, fa0, fb0);
@@ -592,6 +654,46 @@ void gemm_mx_stream_kernel(const uint8_t* __restrict__ A, const uint8_t* __restr
 #pragma unroll
       for (int w = 0; w < SW; ++w) sbC[j][w] = sbN[j][w];
   };
+  // Two-stage step ks on stage cur with the spread schedule: sub-steps 0 .. 2 carry the rest of
+  // bundle ks+1 (into nxt), the last sub-step starts bundle ks+2 (into cur) after the barrier.
+  auto body2 = [&](int ks, uint8_t* cur, uint8_t* nxt) {
+    static_for<BKS>([&](auto sub) {
+      constexpr int S = decltype(sub)::value;
+      if constexpr (S + 1 < BKS) {
+        constexpr int first = S == 0 ? kP3 : S == 1 ? kP3 + kP0 : kP3 + kP0 + kP1;
+        constexpr int cnt = S == 0 ? kP0 : S == 1 ? kP1 : kP2;
+        if constexpr (S % 2 == 0) {
+          lread(cur, S + 1, fa1, fb1);
+          mma_mix(fa0, fb0, saC, sbC, sub, nxt, ks + 1, std::integral_constant<int, first>{},
+                  std::integral_constant<int, cnt>{});
+        } else {
+          lread(cur, S + 1, fa0, fb0);
+          mma_mix(fa1, fb1, saC, sbC, sub, nxt, ks + 1, std::integral_constant<int, first>{},
+                  std::integral_constant<int, cnt>{});
+        }
+      } else {
+        static_assert(BKS % 2 == 0, "last sub-step uses fa1/fb1");
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<0>();
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage ks are done
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        sread(nxt, ks + 1, saN, sbN);
+        lread(nxt, 0, fa0, fb0);
+        mma_mix(fa1, fb1, saC, sbC, sub, cur, ks + 2, std::integral_constant<int, 0>{},
+                std::integral_constant<int, kP3>{});
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+#pragma unroll
+    for (int i = 0; i < FA; ++i)
+#pragma unroll
+      for (int w = 0; w < SW; ++w) saC[i][w] = saN[i][w];
+#pragma unroll
+    for (int j = 0; j < FB; ++j)
+#pragma unroll
+      for (int w = 0; w < SW; ++w) sbC[j][w] = sbN[j][w];
+  };
   int ks = 0;
   if constexpr (STAGES == 4) {
 #pragma unroll 1
@@ -605,38 +707,91 @@ void gemm_mx_stream_kernel(const uint8_t* __restrict__ A, const uint8_t* __restr
     if (ks + 1 < nk) body(ks + 1, stage_ptr(1), stage_ptr(2));
     if (ks + 2 < nk) body(ks + 2, stage_ptr(2), stage_ptr(3));
   } else {
-    // one body per iteration with computed stage pointers: unrolling two steps here doubles
+    // one step per iteration with computed stage pointers: unrolling two steps here doubles
     // the live fragment registers and spills
 #pragma unroll 1
-    for (; ks < nk; ++ks) body(ks, stage_ptr(ks & 1), stage_ptr((ks + 1) & 1));
+    for (; ks < nk; ++ks) body2(ks, stage_ptr(ks & 1), stage_ptr((ks + 1) & 1));
   }
   wait_vmcnt<0>();  // no load may still be writing LDS when the workgroup ends
 
-  // epilogue: acc[i][j][r] = C[m][n], m = wm*32FA + 32 i + (lane % 32),
-  //           n = wn*128 + 32 j + 8 (r / 4) + 4 (lane / 32) + r % 4
+  // Epilogue: acc[i][j][r] = C[m][n], m = wm*32FA + 32 i + (lane % 32),
+  //                                   n = wn*32FB + 32 j + 8 (r / 4) + 4 (lane / 32) + r % 4.
+  // A store straight from that layout writes 16 or 32 bytes into each of 32 rows, and the L2
+  // write-request rate then bounds the kernel's tail. The tile goes through LDS instead (free
+  // now: every wave has passed its last stage read): each wave writes its sub-tile row-major,
+  // then each store instruction writes whole rows (512 or 1024 contiguous bytes). bf16 results
+  // use the hardware round-to-nearest-even pair conversion, which equals rounding the fp32 bit
+  // pattern for every non-NaN input. Rows are padded by 16 bytes so that the 32 rows a write
+  // instruction touches spread over all banks.
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  const bool full = m0 + kBM <= M && n0 + kBN <= N;
+  if (out_bf16) {
+    constexpr int kPitch = kBN * 2 + 16;
+    static_assert(kBM * kPitch <= Cfg::kLds, "bf16 tile fits in LDS");
 #pragma unroll
-  for (int i = 0; i < FA; ++i) {
-    const int64_t m = m0 + wm * 32 * FA + 32 * i + frow;
-    if (m >= M) continue;
+    for (int i = 0; i < FA; ++i)
 #pragma unroll
-    for (int j = 0; j < FB; ++j) {
+      for (int j = 0; j < FB; ++j)
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const int64_t n = n0 + wn * 32 * FB + 32 * j + 8 * rq + 4 * fhalf;
-        if (n >= N) continue;
-        const float v0 = acc[i][j][4 * rq + 0] * alpha_f;
-        const float v1 = acc[i][j][4 * rq + 1] * alpha_f;
-        const float v2 = acc[i][j][4 * rq + 2] * alpha_f;
-        const float v3 = acc[i][j][4 * rq + 3] * alpha_f;
-        if (out_bf16) {
+        for (int rq = 0; rq < 4; ++rq) {
+          const int r = wm * 32 * FA + 32 * i + frow;
+          const int c = wn * 32 * FB + 32 * j + 8 * rq + 4 * fhalf;
+          f32x2 lo = {acc[i][j][4 * rq + 0] * alpha_f, acc[i][j][4 * rq + 1] * alpha_f};
+          f32x2 hi = {acc[i][j][4 * rq + 2] * alpha_f, acc[i][j][4 * rq + 3] * alpha_f};
           uint2 w;
-          w.x = bf16_rne(v0) | (bf16_rne(v1) << 16);
-          w.y = bf16_rne(v2) | (bf16_rne(v3) << 16);
-          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(C) + m * ldc + n) = w;
-        } else {
-          *reinterpret_cast<float4*>(reinterpret_cast<float*>(C) + m * ldc + n) =
-              make_float4(v0, v1, v2, v3);
+          w.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
+          w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2));
+          *reinterpret_cast<uint2*>(smem + r * kPitch + 2 * c) = w;
         }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    // instruction q of wave w: rows 2 (q WAVES + w) + lane / 32, 16-byte chunk lane % 32
+    constexpr int kReads = kBM / 2 / WAVES;
+#pragma unroll 8
+    for (int q = 0; q < kReads; ++q) {
+      const int r = 2 * (q * WAVES + wave) + fhalf;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(smem + r * kPitch + 16 * frow);
+      const int64_t m = m0 + r, n = n0 + 8 * frow;
+      if (full || (m < M && n < N))
+        *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(C) + m * ldc + n) = v;
+    }
+  } else {
+    // fp32: two passes of 128 rows (the waves with wm == p fill pass p)
+    constexpr int kPitch = kBN * 4 + 16;
+    constexpr int kPassRows = kBM / 2;
+    static_assert(kPassRows * kPitch <= Cfg::kLds, "fp32 half tile fits in LDS");
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      if ((wm * 32 * FA) / kPassRows == p) {
+#pragma unroll
+        for (int i = 0; i < FA; ++i)
+#pragma unroll
+          for (int j = 0; j < FB; ++j)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+              const int r = wm * 32 * FA + 32 * i + frow - p * kPassRows;
+              const int c = wn * 32 * FB + 32 * j + 8 * rq + 4 * fhalf;
+              *reinterpret_cast<f32x4*>(smem + r * kPitch + 4 * c) =
+                  f32x4{acc[i][j][4 * rq + 0] * alpha_f, acc[i][j][4 * rq + 1] * alpha_f,
+                        acc[i][j][4 * rq + 2] * alpha_f, acc[i][j][4 * rq + 3] * alpha_f};
+            }
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_s_barrier();
+      // instruction q of wave w: row q WAVES + w, 16-byte chunk lane
+      constexpr int kReads = kPassRows / WAVES;
+#pragma unroll 8
+      for (int q = 0; q < kReads; ++q) {
+        const int r = q * WAVES + wave;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(smem + r * kPitch + 16 * lane);
+        const int64_t m = m0 + p * kPassRows + r, n = n0 + 4 * lane;
+        if (full || (m < M && n < N))
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(C) + m * ldc + n) = v;
+      }
+      if (p == 0) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_s_barrier();
       }
     }
   }
@@ -652,9 +807,13 @@ hipError_t mx_launch_gemm(const GemmArgs& g) {
   const float alpha_f = __builtin_bit_cast(float, (uint32_t)(g.alpha + 127) << 23);
   const int lga = g.ga == 32 ? 5 : 0, lgb = g.gb == 32 ? 5 : 0;
   const dim3 grid((unsigned)(nbm * nbn));
+  // loads of a step issued during sub-steps 3, 0, 1 (the rest during sub-step 2): as early as
+  // the at-most-one-load-per-MFMA-pair rule allows
+  constexpr int kS3 = kStreamWaves == 4 ? 8 : 4, kS0 = kStreamWaves == 4 ? 8 : 4;
+  constexpr int kS1 = kStreamWaves == 4 ? 1 : 2;
   if (g.K % 512 == 0 && g.K > 0)
-    hipLaunchKernelGGL((gemm_mx_stream_kernel<kStreamWaves, 4, 2>), grid, dim3(64 * kStreamWaves), 0,
-                       (hipStream_t)g.stream, g.a,
+    hipLaunchKernelGGL((gemm_mx_stream_kernel<kStreamWaves, 4, 2, kS3, kS0, kS1>), grid,
+                       dim3(64 * kStreamWaves), 0, (hipStream_t)g.stream, g.a,
                        g.as, lga, g.b, g.bs, lgb, g.M, g.N, g.K, alpha_f, g.out_bf16 ? 1 : 0, g.c,
                        g.ldc, (int)nbm, (int)nbn);
   else if (g.K % kBK == 0 && g.K > 0)
