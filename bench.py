@@ -49,6 +49,10 @@ def parse():
                    help="source rows per operand quantization in the CPU oracle sample")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also launch one plain 1 GiB device copy (counter calibration runs)")
+    p.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="no GPU work: turn the counter_collection.csv files of a FETCH_SIZE and "
+                        "a WRITE_SIZE rocprofv3 pass over a --copy-calibration run into the "
+                        "per-launch HBM traffic record that later runs report")
     return p.parse_args()
 
 
@@ -173,8 +177,75 @@ def load_traffic(launch_flops_key: str):
     return rec.get(launch_flops_key)
 
 
+COPY_BYTES = 1 << 30  # the --copy-calibration copy reads and writes 1 GiB
+
+
+def counter_values(path: str, counter: str):
+    """Per-dispatch values of `counter` from a rocprofv3 counter_collection.csv (summed over the
+    hardware instances of each dispatch), grouped by (kernel name, workgroup count)."""
+    import collections
+    import csv
+    per = collections.defaultdict(float)
+    key_of = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        d = int(r["Dispatch_Id"])
+        per[d] += float(r["Counter_Value"])
+        key_of[d] = (r["Kernel_Name"], int(r["Grid_Size"]) // max(int(r["Workgroup_Size"]), 1))
+    out = collections.defaultdict(list)
+    for d, v in per.items():
+        out[key_of[d]].append(v)
+    return out
+
+
+def write_traffic(fetch_csv: str, write_csv: str, workload: str):
+    """HBM bytes per launch of each GEMM from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each
+    scaled by what the same counter reads for the plain 1 GiB copy of the calibration run."""
+    if workload != "llama70b_down":
+        raise SystemExit("traffic records are kept for the llama70b_down workload")
+    T, K, N = 16384, 28672, 8192  # tokens, FFN (Fprop reduction), hidden
+    fetch, write = counter_values(fetch_csv, "FETCH_SIZE"), counter_values(write_csv, "WRITE_SIZE")
+
+    def copy_value(table):
+        # the calibration copy is the largest device-to-device copy dispatch of the run
+        vals = [v for (name, _), vs in table.items() if "copyBuffer" in name for v in vs]
+        if not vals:
+            raise SystemExit("no copy kernel in the counter file (run with --copy-calibration)")
+        return max(vals)
+
+    ff = COPY_BYTES / (copy_value(fetch) * 1024.0)
+    wf = COPY_BYTES / (copy_value(write) * 1024.0)
+
+    def gemm_value(table, wgs):
+        vals = [vs for (name, g), vs in table.items() if "gemm_mx" in name and g == wgs]
+        if len(vals) != 1:
+            raise SystemExit(f"expected one GEMM kernel with {wgs} workgroups, found {len(vals)}")
+        return sum(vals[0]) / len(vals[0])
+
+    rec = {"gemm_sha": sha(GEMM_SRC), "fetch_factor": ff, "write_factor": wf,
+           "command_fetch": ("rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch "
+                             "-o run -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline "
+                             "--copy-calibration"),
+           "command_write": ("rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write "
+                             "-o run -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline "
+                             "--copy-calibration")}
+    for name, M, Nn, Kk in (("fprop", T, N, K), ("dgrad", T, K, N), ("wgrad", N, K, T)):
+        wgs = ((M + 255) // 256) * ((Nn + 255) // 256)
+        hbm = gemm_value(fetch, wgs) * 1024.0 * ff + gemm_value(write, wgs) * 1024.0 * wf
+        alg = (M + Nn) * (Kk // 2 + Kk // 32) + 2 * M * Nn  # both operands with scales + bf16 C
+        rec[f"{name}_hbm_bytes_per_launch"] = int(round(hbm))
+        rec[f"{name}_algorithmic_bytes_per_launch"] = int(alg)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
 def main():
     args = parse()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic, args.workload)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               "(the path's multi-GPU sharding is described in DESIGN.md, not built)",
