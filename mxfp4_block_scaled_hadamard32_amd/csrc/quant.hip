@@ -252,23 +252,16 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
   }
   __syncthreads();
 
-  // codes: thread t writes half (t & 1) of column t >> 1 (+128 per round): row blocks
-  // 4 h .. 4 h + 3, 16 B each
+  // codes: 8 lanes per column, 16 bytes (one row block) each, so that one store instruction
+  // writes the whole 128-byte pieces of 8 columns
   const int64_t rows2 = rows / 2;
 #pragma unroll
-  for (int round = 0; round < kColHalves; ++round) {
-    const int c = round * 128 + (threadIdx.x >> 1), h = threadIdx.x & 1;
-    if (ctile0 + c < cols) {
-      uint8_t* dst = codes_t + (ctile0 + c) * rows2 + rb0 * 16;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rbl = 4 * h + i;
-        if (rbl < nrb)
-          __builtin_nontemporal_store(
-              *reinterpret_cast<const u32x4*>(ctile + c * kCodeStride + rbl * 16),
-              reinterpret_cast<u32x4*>(dst + rbl * 16));
-      }
-    }
+  for (int round = 0; round < kColTileCols * 8 / kThreads; ++round) {
+    const int c = round * (kThreads / 8) + (threadIdx.x >> 3), rbl = threadIdx.x & 7;
+    if (ctile0 + c < cols && rbl < nrb)
+      __builtin_nontemporal_store(
+          *reinterpret_cast<const u32x4*>(ctile + c * kCodeStride + rbl * 16),
+          reinterpret_cast<u32x4*>(codes_t + (ctile0 + c) * rows2 + rb0 * 16 + rbl * 16));
   }
   // scales: thread t writes the nrb scale bytes of column t (+256 per round)
   for (int cs = threadIdx.x; cs < kColTileCols; cs += kThreads) {
@@ -286,71 +279,107 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
 // ---------------------------------------------------------------------------------------------
 // 32x32 tiles: one scale per tile from the tile maximum; every element is rounded once and
 // written to the row-major codes and (optionally) to the K-major codes of the transpose.
-// Lane = 16 * tile + 4 * column-group + q; the 16 lanes of a tile are one DPP row.
+// A workgroup owns 256 rows x 256 columns (8 x 8 tiles). Pass p of wave w covers row block
+// (p & 1) * 4 + w and the 128-column half p >> 1; there lane = 16 * tile + 4 * column-group + q
+// holds the 8x8 patch at rows 8q.., columns 8 (4 tile + column-group).., so the 16 lanes of a
+// tile are one DPP row. Both code layouts are assembled in LDS and leave as whole 128-byte rows.
 // ---------------------------------------------------------------------------------------------
+constexpr int k2dTile = 256;
+constexpr int k2dStride = 144;  // LDS bytes per row (row-major) or column (transposed) + padding
+
 template <bool BF16, bool SR, bool CEIL>
 __global__ __launch_bounds__(kThreads) void quant_2d_kernel(
     const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, uint64_t seed,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, uint8_t* __restrict__ codes_t,
-    uint8_t* __restrict__ scales_t) {
-  const int lane = threadIdx.x & 63;
-  const int q = lane & 3;
-  const int64_t rb = (int64_t)blockIdx.y * 4 + (threadIdx.x >> 6);
-  const int64_t c0 = (int64_t)blockIdx.x * 128 + (lane >> 2) * 8;
-  if (rb >= rows / 32 || c0 >= cols) return;  // whole tiles leave together (cols % 32 == 0)
-  const int64_t r0 = rb * 32 + 8 * q;
+    uint8_t* __restrict__ scales_t, int64_t n_ct) {
+  __shared__ __attribute__((aligned(16))) uint8_t rtile[k2dTile * k2dStride];  // [row][col/2]
+  __shared__ __attribute__((aligned(16))) uint8_t ttile[k2dTile * k2dStride];  // [col][row/2]
+  __shared__ uint8_t stile[64];                                                 // [rb][cb]
+  const int64_t rt = blockIdx.x / n_ct, ct = blockIdx.x - rt * n_ct;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int q = lane & 3, cgl = lane >> 2;  // cgl = 4 * tile + column-group, 0..15
+  const int64_t rtile0 = rt * k2dTile, ctile0 = ct * k2dTile;
+  const int nrb = (int)min((int64_t)8, rows / 32 - rt * 8);
+  const int ncb = (int)min((int64_t)8, cols / 32 - ct * 8);
 
-  float p[8][8];
-  load_patch<BF16>(x, ld, r0, c0, p);
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int rbl = (pass & 1) * 4 + wave, ch = pass >> 1;
+    const int cl0 = ch * 128 + cgl * 8;  // first column of the patch within the tile
+    if (rbl >= nrb || cl0 >= ncb * 32) continue;  // whole 32x32 tiles leave together
+    const int64_t r0 = rtile0 + rbl * 32 + 8 * q, c0 = ctile0 + cl0;
+    float p[8][8];
+    load_patch<BF16>(x, ld, r0, c0, p);
 
-  uint32_t m = 0;
+    uint32_t m = 0;
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-    for (int k = 0; k < 8; ++k) m = max(m, abs_bits(p[j][k]));
-  m = max(m, dpp_u32<kQuadXor1>(m));
-  m = max(m, dpp_u32<kQuadXor2>(m));
-  m = max(m, dpp_u32<kRowRor4>(m));
-  m = max(m, dpp_u32<kRowRor8>(m));
-  const uint32_t sb = scale_byte<CEIL>(m);
+      for (int k = 0; k < 8; ++k) m = max(m, abs_bits(p[j][k]));
+    m = max(m, dpp_u32<kQuadXor1>(m));
+    m = max(m, dpp_u32<kQuadXor2>(m));
+    m = max(m, dpp_u32<kRowRor4>(m));
+    m = max(m, dpp_u32<kRowRor8>(m));
+    const uint32_t sb = scale_byte<CEIL>(m);
 
-  uint32_t R[8];  // R[j] = codes of patch row j (nibble k = column k)
-  if (sb == 0xFFu) {
+    uint32_t R[8];  // R[j] = codes of patch row j (nibble k = column k)
+    if (sb == 0xFFu) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) R[j] = 0;
-  } else {
-    const float inv = inv_scale_from_byte(sb);
+      for (int j = 0; j < 8; ++j) R[j] = 0;
+    } else {
+      const float inv = inv_scale_from_byte(sb);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < 8; ++j) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) p[j][k] = p[j][k] * inv;
-      if (SR) {
-        uint32_t r[8];
-        sr_fields8((uint64_t)((r0 + j) * cols + c0) >> 3, seed, r);
-        uint32_t word = 0;
+        for (int k = 0; k < 8; ++k) p[j][k] = p[j][k] * inv;
+        if (SR) {
+          uint32_t r[8];
+          sr_fields8((uint64_t)((r0 + j) * cols + c0) >> 3, seed, r);
+          uint32_t word = 0;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) word |= e2m1_sr_code(p[j][k], r[k]) << (4 * k);
-        R[j] = word;
-      } else {
-        R[j] = cvt_rne_pack8(p[j]);
+          for (int k = 0; k < 8; ++k) word |= e2m1_sr_code(p[j][k], r[k]) << (4 * k);
+          R[j] = word;
+        } else {
+          R[j] = cvt_rne_pack8(p[j]);
+        }
       }
     }
-  }
-  const int64_t cols2 = cols / 2;
+    const int rl0 = rbl * 32 + 8 * q;  // first row of the patch within the tile
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    __builtin_nontemporal_store(R[j], reinterpret_cast<uint32_t*>(codes + (r0 + j) * cols2 + c0 / 2));
-  if (codes_t) {
+    for (int j = 0; j < 8; ++j)
+      *reinterpret_cast<uint32_t*>(rtile + (rl0 + j) * k2dStride + cl0 / 2) = R[j];
     transpose_nibbles8x8(R);  // R[k] = codes of patch column k (nibble j = row j)
-    const int64_t rows2 = rows / 2;
 #pragma unroll
     for (int k = 0; k < 8; ++k)
-      __builtin_nontemporal_store(R[k], reinterpret_cast<uint32_t*>(codes_t + (c0 + k) * rows2 + r0 / 2));
+      *reinterpret_cast<uint32_t*>(ttile + (cl0 + k) * k2dStride + rl0 / 2) = R[k];
+    if ((lane & 15) == 0) stile[rbl * 8 + cl0 / 32] = (uint8_t)sb;
   }
-  if ((lane & 15) == 0) {
-    const int64_t tc = c0 / 32;
-    scales[rb * (cols / 32) + tc] = (uint8_t)sb;
-    if (scales_t) scales_t[tc * (rows / 32) + rb] = (uint8_t)sb;
+  __syncthreads();
+
+  // codes: 8 lanes per row (column) of the tile, 16 bytes each: every store instruction writes
+  // the whole 128-byte pieces of 8 rows
+  const int64_t cols2 = cols / 2, rows2 = rows / 2;
+  const int seg = threadIdx.x & 7;
+#pragma unroll
+  for (int round = 0; round < k2dTile * 8 / kThreads; ++round) {
+    const int i = round * (kThreads / 8) + (threadIdx.x >> 3);
+    if (i < nrb * 32 && seg < ncb)  // a 32-column block is one 16-byte segment
+      __builtin_nontemporal_store(
+          *reinterpret_cast<const u32x4*>(rtile + i * k2dStride + 16 * seg),
+          reinterpret_cast<u32x4*>(codes + (rtile0 + i) * cols2 + ctile0 / 2 + 16 * seg));
+    if (codes_t && i < ncb * 32 && seg < nrb)
+      __builtin_nontemporal_store(
+          *reinterpret_cast<const u32x4*>(ttile + i * k2dStride + 16 * seg),
+          reinterpret_cast<u32x4*>(codes_t + (ctile0 + i) * rows2 + rtile0 / 2 + 16 * seg));
+  }
+  // scales: thread t < 64 writes tile (t / 8, t % 8) to both layouts
+  if (threadIdx.x < 64) {
+    const int rbl = threadIdx.x >> 3, cbl = threadIdx.x & 7;
+    if (rbl < nrb && cbl < ncb) {
+      const uint8_t sb = stile[rbl * 8 + cbl];
+      scales[(rt * 8 + rbl) * (cols / 32) + ct * 8 + cbl] = sb;
+      if (scales_t) scales_t[(ct * 8 + cbl) * (rows / 32) + rt * 8 + rbl] = sb;
+    }
   }
 }
 
@@ -438,11 +467,11 @@ hipError_t launch_cols(const QuantArgs& a) {
 
 template <bool BF16, bool SR, bool CEIL>
 hipError_t launch_2d(const QuantArgs& a) {
-  const dim3 grid((unsigned)((a.cols + 127) / 128), (unsigned)((a.rows / 32 + 3) / 4));
-  if (grid.y > 65535u) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((quant_2d_kernel<BF16, SR, CEIL>), grid, dim3(kThreads), 0,
-                     (hipStream_t)a.stream, a.x, a.rows, a.cols, a.ld, a.seed, a.codes, a.scales,
-                     a.codes_t, a.scales_t);
+  const int64_t n_rt = (a.rows + k2dTile - 1) / k2dTile, n_ct = (a.cols + k2dTile - 1) / k2dTile;
+  if (n_rt * n_ct > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((quant_2d_kernel<BF16, SR, CEIL>), dim3((unsigned)(n_rt * n_ct)), dim3(kThreads),
+                     0, (hipStream_t)a.stream, a.x, a.rows, a.cols, a.ld, a.seed, a.codes, a.scales,
+                     a.codes_t, a.scales_t, n_ct);
   return hipGetLastError();
 }
 

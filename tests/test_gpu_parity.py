@@ -53,6 +53,7 @@ QUANT_CASES = [
     (64, 96, 0, torch.bfloat16),
     (96, 136, 0, torch.float32),    # cols not a multiple of 128 (ragged lane groups)
     (160, 392, 0, torch.bfloat16),
+    (544, 264, 0, torch.bfloat16),  # three 256-row tiles, the last partial; ragged columns
 ]
 OPTS = [
     # scale_rule, round, hadamard, sign_mask
@@ -105,7 +106,8 @@ def test_non_finite_block(mx, orc):
 
 
 @pytest.mark.parametrize("rows,cols,dtype", [(64, 64, torch.bfloat16), (96, 160, torch.float32),
-                                             (256, 384, torch.bfloat16)])
+                                             (256, 384, torch.bfloat16),
+                                             (288, 544, torch.bfloat16)])  # partial 256x256 tiles
 @pytest.mark.parametrize("rule,rnd", [(1, 0), (1, 1), (0, 0)])
 def test_quantize_2d_bit_exact(mx, orc, rows, cols, dtype, rule, rnd):
     x = special_input(rows, cols, dtype, seed=rows + cols)
