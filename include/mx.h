@@ -101,7 +101,12 @@ typedef struct {
  * sign_mask and apply the unnormalised 32-point Sylvester-Hadamard transform
  * H[i][j] = (-1)^popcount(i & j) as five fp32 butterfly stages of span 1, 2, 4, 8, 16;
  * block maximum; scale exponent; v = x * 2^-e in fp32; round; pack.
- * Returns MX_ERR_UNSUPPORTED for nothing; MX_ERR_ARG for a bad dtype/axis/option. */
+ * Alignment: x and every source row (ld * element size) 16 bytes; codes 4 bytes (axis = 1) or
+ * 16 bytes (axis = 0); axis = 0 also needs cols % 8 == 0.
+ * Errors (nothing is launched): MX_ERR_NULL for a NULL x, codes, scales or opts;
+ * MX_ERR_SHAPE for negative sizes, ld < cols or a multiple-of-32 / row-alignment rule;
+ * MX_ERR_ARG for a bad dtype, axis or option value, or a misaligned pointer;
+ * MX_ERR_LAUNCH if the kernel launch fails. rows == 0 or cols == 0 is a no-op. */
 mx_status mx_quantize(const void* x, int32_t dtype, int64_t rows, int64_t cols, int64_t ld,
                       int32_t axis, const mx_quant_opts* opts, uint8_t* codes, uint8_t* scales,
                       void* stream);
@@ -112,7 +117,9 @@ mx_status mx_quantize(const void* x, int32_t dtype, int64_t rows, int64_t cols, 
  * codes  [rows][cols/2], scales   [rows/32][cols/32]      (required)
  * codes_t[cols][rows/2], scales_t [cols/32][rows/32]      (optional, may be NULL)
  * codes_t/scales_t hold the SAME rounding decisions in the K-major layout of X^T, so the
- * transposed GEMM consumes them without re-quantization. */
+ * transposed GEMM consumes them without re-quantization.
+ * Alignment: x and every source row 16 bytes, codes and codes_t 16 bytes. Errors as for
+ * mx_quantize, plus MX_ERR_NULL when exactly one of codes_t / scales_t is NULL. */
 mx_status mx_quantize_2d(const void* x, int32_t dtype, int64_t rows, int64_t cols, int64_t ld,
                          const mx_quant_opts* opts, uint8_t* codes, uint8_t* scales,
                          uint8_t* codes_t, uint8_t* scales_t, void* stream);
@@ -121,7 +128,9 @@ mx_status mx_quantize_2d(const void* x, int32_t dtype, int64_t rows, int64_t col
  * ..."]); out is [rows][cols] contiguous. block_rows = 1 reads scales [rows][cols/32];
  * block_rows = 32 reads 2-D scales [rows/32][cols/32]. If inv_hadamard (block_rows == 1 only),
  * each 32-block is then mapped back by (1/32) * D * H: the same five fp32 butterfly stages,
- * a multiply by 1/32, and the sign flips of sign_mask. */
+ * a multiply by 1/32, and the sign flips of sign_mask.
+ * Alignment: codes 4 bytes, out 16 bytes; cols % 32 == 0 (rows % 32 == 0 for block_rows = 32).
+ * MX_ERR_UNSUPPORTED for inv_hadamard with block_rows = 32. */
 mx_status mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
                         int32_t block_rows, int32_t inv_hadamard, uint32_t sign_mask, float* out,
                         void* stream);
@@ -136,7 +145,11 @@ mx_status mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t row
  *   fprop: Y  [T][N] = X  [T][K] . W [N][K]^T   (reduce over K)
  *   dgrad: dX [T][K] = dY [T][N] . Wt[K][N]^T   (reduce over N; Wt = W blocked along N)
  *   wgrad: dW [N][K] = dYt[N][T] . Xt[K][T]^T   (reduce over tokens T)
- * M, N multiples of 32, K a multiple of 32. */
+ * M, N multiples of 32, K a multiple of 32; the operand codes and C 16-byte aligned, ldc a
+ * multiple of 8 elements. One 256-row operand tile must stay below 2 GiB (256 * K / 2 < 2^31).
+ * Errors (nothing is launched): MX_ERR_SHAPE, MX_ERR_ARG (granularity, out_dtype, alpha_exp
+ * outside [-126, 127], alignment), MX_ERR_NULL; MX_ERR_LAUNCH if the launch fails or the shape
+ * exceeds the 32-bit offsets above. M == 0 or N == 0 is a no-op; K == 0 writes zeros. */
 mx_status mx_gemm_fprop(const uint8_t* xq, const uint8_t* xs, int32_t gx, const uint8_t* wq,
                         const uint8_t* ws, int32_t gw, int64_t T, int64_t N, int64_t K,
                         int32_t alpha_exp, int32_t out_dtype, void* y, int64_t ldy, void* stream);

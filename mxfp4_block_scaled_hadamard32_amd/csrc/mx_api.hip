@@ -64,7 +64,8 @@ mx_status mx_quantize(const void* x, int32_t dtype, int64_t rows, int64_t cols, 
   if (axis == 0 && (rows % 32 != 0 || cols % 8 != 0)) return MX_ERR_SHAPE;
   if (rows == 0 || cols == 0) return MX_OK;
   if (!x || !codes || !scales) return MX_ERR_NULL;
-  if (!aligned(codes, 4)) return MX_ERR_ARG;
+  // rows: one dword of codes per lane; columns: 16-byte pieces of transposed code rows
+  if (!aligned(codes, axis == 1 ? 4 : 16)) return MX_ERR_ARG;
   QuantArgs a{x, dtype == MX_BF16, rows, cols, ld, axis, opts->scale_rule == MX_SCALE_CEIL,
               opts->round == MX_ROUND_SR, opts->hadamard == 1, opts->sign_mask, opts->seed,
               codes, scales, nullptr, nullptr, stream};
@@ -82,7 +83,7 @@ mx_status mx_quantize_2d(const void* x, int32_t dtype, int64_t rows, int64_t col
   if ((codes_t == nullptr) != (scales_t == nullptr)) return MX_ERR_NULL;
   if (rows == 0 || cols == 0) return MX_OK;
   if (!x || !codes || !scales) return MX_ERR_NULL;
-  if (!aligned(codes, 4) || (codes_t && !aligned(codes_t, 4))) return MX_ERR_ARG;
+  if (!aligned(codes, 16) || (codes_t && !aligned(codes_t, 16))) return MX_ERR_ARG;
   QuantArgs a{x, dtype == MX_BF16, rows, cols, ld, 1, opts->scale_rule == MX_SCALE_CEIL,
               opts->round == MX_ROUND_SR, false, 0u, opts->seed, codes, scales, codes_t,
               scales_t, stream};

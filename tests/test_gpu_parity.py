@@ -241,6 +241,10 @@ def test_empty_inputs_are_noops(mx):
                            torch.zeros((32, 32), dtype=torch.uint8, device=DEV),
                            torch.zeros((32, 2), dtype=torch.uint8, device=DEV), 1)
     assert out.shape == (0, 32)
+    # K == 0: an empty reduction, every output is zero
+    z = torch.empty((32, 0), dtype=torch.uint8, device=DEV)
+    out = mx.mx_gemm_fprop(z, z, 1, z, z, 1, out=torch.full((32, 32), 7.0, device=DEV))
+    assert torch.count_nonzero(out).item() == 0
 
 
 def test_bad_shape_raises(mx):
