@@ -99,12 +99,16 @@ __device__ __forceinline__ float inv_scale_from_byte(uint32_t byte) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// E2M1 rounding.
-// RNE: gfx950's converter (v_cvt_scalef32_pk_fp4_f32) with unit scale rounds to nearest with
-//      ties to the even code, saturates at 6 and copies the sign, as the definition requires.
-// SR : in software. a = min(|v|, 6); the grid step q around a is 0.5 below 2 and 2^(E-1) above
-//      (E = exponent of a); t = a / q is exact, lo index = floor(t), f = t - floor(t), and the
-//      magnitude rounds up iff r < f * 65536 with r the element's 16-bit random field.
+// E2M1 rounding. Both use gfx950's converters with unit scale (v is already x * 2^-e in fp32);
+// they saturate at 6 and copy the sign.
+// RNE: v_cvt_scalef32_pk_fp4_f32 rounds to nearest with ties to the even code.
+// SR : v_cvt_scalef32_sr_pk_fp4_f32 adds the random word's bits below the kept precision of
+//      |v| on the grid and truncates (dithered truncation). The first value of the pair reads
+//      the word from its top bit down; with the element's 16-bit field in the top half and the
+//      low half zero that is exactly: round up iff f * 2^16 + r >= 2^16, f the position of |v|
+//      between its grid neighbours. Only the first value of each pair is used (the second one
+//      reads the same word shifted by one bit, so pairs would share their random bits); its
+//      partner is 0, which encodes as 0.
 // ---------------------------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t cvt_rne_pack8(const float (&v)[8]) {
   uint32_t w = 0;
@@ -115,18 +119,21 @@ __device__ __forceinline__ uint32_t cvt_rne_pack8(const float (&v)[8]) {
   return w;
 }
 
-__device__ __forceinline__ uint32_t e2m1_sr_code(float v, uint32_t r16) {
-  const float a = fminf(fabsf(v), 6.0f);
-  const uint32_t ub = __float_as_uint(a);
-  int32_t qb = (int32_t)(ub & 0x7F800000u) - 0x00800000;
-  qb = qb > 0x3F000000 ? qb : 0x3F000000;             // step 2^(E-1), at least 0.5
-  const float inv_q = __uint_as_float(0x7F000000u - (uint32_t)qb);
-  const float t = a * inv_q;                           // exact
-  const float fl = floorf(t);
-  const float fr = t - fl;                             // exact
-  const uint32_t up = ((float)r16 < fr * 65536.0f) ? 1u : 0u;
-  const uint32_t idx = (uint32_t)fl + up + ((uint32_t)qb >> 22) - 252u;
-  return idx | ((__float_as_uint(v) >> 28) & 8u);
+// rt[k]: the random field of value k in bits 31..16, zeros below. Each conversion writes its
+// code pair to byte 0, value k in the low nibble; the pair's second value is just the next
+// register (its code is discarded), and the nibble is placed by hand (the compiler does not
+// carry the untouched bytes of the destination through this builtin, so byte selection
+// cannot accumulate a word).
+__device__ __forceinline__ uint32_t cvt_sr_pack8(const float (&v)[8], const uint32_t (&rt)[8]) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  uint32_t w = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const f32x2_t pair = {v[k], v[k < 7 ? k + 1 : k]};
+    const uint32_t b = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, pair, rt[k], 1.0f, 0);
+    w |= (b & 0xFu) << (4 * k);
+  }
+  return w;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -152,14 +159,16 @@ __device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
   return make_uint4(c0, c1, c2, c3);
 }
 
-// Eight 16-bit random fields for source elements 8g .. 8g+7 (field k for element 8g + k).
-__device__ __forceinline__ void sr_fields8(uint64_t g, uint64_t seed, uint32_t (&r)[8]) {
+// Random words for source elements 8g .. 8g+7: field k (16 bits) of the Philox output at
+// counter g, placed in bits 31..16 of rt[k] (field k is the low half of output word k / 2 for
+// even k, the high half for odd k).
+__device__ __forceinline__ void sr_top8(uint64_t g, uint64_t seed, uint32_t (&rt)[8]) {
   const uint4 w = philox4x32_10((uint32_t)g, (uint32_t)(g >> 32), 0u, 0u, (uint32_t)seed,
                                 (uint32_t)(seed >> 32));
-  r[0] = w.x & 0xFFFFu; r[1] = w.x >> 16;
-  r[2] = w.y & 0xFFFFu; r[3] = w.y >> 16;
-  r[4] = w.z & 0xFFFFu; r[5] = w.z >> 16;
-  r[6] = w.w & 0xFFFFu; r[7] = w.w >> 16;
+  rt[0] = w.x << 16; rt[1] = w.x & 0xFFFF0000u;
+  rt[2] = w.y << 16; rt[3] = w.y & 0xFFFF0000u;
+  rt[4] = w.z << 16; rt[5] = w.z & 0xFFFF0000u;
+  rt[6] = w.w << 16; rt[7] = w.w & 0xFFFF0000u;
 }
 
 // ---------------------------------------------------------------------------------------------

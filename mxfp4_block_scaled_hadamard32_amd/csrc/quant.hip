@@ -102,10 +102,9 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
 #pragma unroll
       for (int k = 0; k < 8; ++k) w[k] = w[k] * inv;
       if (SR) {
-        uint32_t r[8];
-        sr_fields8((uint64_t)g, seed, r);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) word |= e2m1_sr_code(w[k], r[k]) << (4 * k);
+        uint32_t rt[8];
+        sr_top8((uint64_t)g, seed, rt);
+        word = cvt_sr_pack8(w, rt);
       } else {
         word = cvt_rne_pack8(w);
       }
@@ -225,10 +224,10 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
       m = max(m, dpp_u32<kQuadXor2>(m));
       sb[k] = scale_byte<CEIL>(m);
     }
-    uint32_t r[8][8];
+    uint32_t r[8][8];  // r[j][k]: random word of patch element (j, k)
     if (SR) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) sr_fields8((uint64_t)((r0 + j) * cols + c0) >> 3, seed, r[j]);
+      for (int j = 0; j < 8; ++j) sr_top8((uint64_t)((r0 + j) * cols + c0) >> 3, seed, r[j]);
     }
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -239,8 +238,10 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
 #pragma unroll
         for (int j = 0; j < 8; ++j) col[j] = p[j][k] * inv;
         if (SR) {
+          uint32_t rc[8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) word |= e2m1_sr_code(col[j], r[j][k]) << (4 * j);
+          for (int j = 0; j < 8; ++j) rc[j] = r[j][k];
+          word = cvt_sr_pack8(col, rc);
         } else {
           word = cvt_rne_pack8(col);
         }
@@ -333,12 +334,9 @@ __global__ __launch_bounds__(kThreads) void quant_2d_kernel(
 #pragma unroll
         for (int k = 0; k < 8; ++k) p[j][k] = p[j][k] * inv;
         if (SR) {
-          uint32_t r[8];
-          sr_fields8((uint64_t)((r0 + j) * cols + c0) >> 3, seed, r);
-          uint32_t word = 0;
-#pragma unroll
-          for (int k = 0; k < 8; ++k) word |= e2m1_sr_code(p[j][k], r[k]) << (4 * k);
-          R[j] = word;
+          uint32_t rt[8];
+          sr_top8((uint64_t)((r0 + j) * cols + c0) >> 3, seed, rt);
+          R[j] = cvt_sr_pack8(p[j], rt);
         } else {
           R[j] = cvt_rne_pack8(p[j]);
         }
