@@ -71,13 +71,10 @@ typedef enum { MX_SCALE_FLOOR = 0, MX_SCALE_CEIL = 1 } mx_scale_rule;
 
 /* Rounding of v = x * 2^-e to E2M1:
  *  MX_ROUND_RNE: nearest grid point, ties to the even code, |v| >= 6 saturates to 6.
- *  MX_ROUND_SR : dithered truncation: with lo <= |v| < hi adjacent grid points and
- *                f = (|v| - lo) / (hi - lo), the magnitude rounds up to hi iff f + r / 2^16 >= 1,
- *                where r is the 16-bit random field of the element, i.e. it rounds up for
- *                floor(f * 2^16) of the 2^16 values of r; so E[round(v)] = v up to 2^-16 of a
- *                grid step [P3, "The fix ..."; P4]. This is the rule of gfx950's stochastic
- *                FP4 converter, which the path uses [P1 paragraph 1: hardware-assisted
- *                stochastic rounding]. r comes from Philox4x32-10 (Salmon et al., SC'11) keyed by
+ *  MX_ROUND_SR : with lo <= |v| < hi adjacent grid points and f = (|v| - lo) / (hi - lo), the
+ *                magnitude rounds up to hi iff r < f * 2^16, where r is the 16-bit random field
+ *                of the element; so E[round(v)] = v up to 2^-16 of a grid step [P3, "The fix
+ *                ..."; P4]. r comes from Philox4x32-10 (Salmon et al., SC'11) keyed by
  *                (seed & 0xffffffff, seed >> 32) at counter (i >> 3 as two 32-bit words, 0, 0);
  *                element i takes 16-bit field (i & 7) of the 128-bit output: word (i & 7) >> 1,
  *                low half for even i. i is the row-major index r * cols + c of the element in

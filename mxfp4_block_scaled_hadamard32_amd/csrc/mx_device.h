@@ -99,16 +99,20 @@ __device__ __forceinline__ float inv_scale_from_byte(uint32_t byte) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// E2M1 rounding. Both use gfx950's converters with unit scale (v is already x * 2^-e in fp32);
-// they saturate at 6 and copy the sign.
-// RNE: v_cvt_scalef32_pk_fp4_f32 rounds to nearest with ties to the even code.
-// SR : v_cvt_scalef32_sr_pk_fp4_f32 adds the random word's bits below the kept precision of
-//      |v| on the grid and truncates (dithered truncation). The first value of the pair reads
-//      the word from its top bit down; with the element's 16-bit field in the top half and the
-//      low half zero that is exactly: round up iff f * 2^16 + r >= 2^16, f the position of |v|
-//      between its grid neighbours. Only the first value of each pair is used (the second one
-//      reads the same word shifted by one bit, so pairs would share their random bits); its
-//      partner is 0, which encodes as 0.
+// E2M1 rounding of v = x * 2^-e (already computed in fp32); both saturate at 6 and copy the sign.
+// RNE: gfx950's v_cvt_scalef32_pk_fp4_f32 with unit scale rounds to nearest with ties to the
+//      even code, as the definition requires.
+// SR : round up iff r < f * 2^16 (r the element's 16-bit random field, f the position of |v|
+//      between its two grid neighbours). gfx950's stochastic converter
+//      (v_cvt_scalef32_sr_pk_fp4_f32) rounds the first value of its pair up iff
+//      floor(f * 2^22) + (R >> 10) >= 2^22 for its random word R. With R = (~r << 16) | 0xFFFF
+//      that is floor(f * 2^22) > 64 r, while the rule wants f * 2^22 > 64 r, i.e.
+//      ceil(f * 2^22) > 64 r. The two agree once f * 2^22 is an integer: the value is first
+//      rounded up (in magnitude) to a multiple of 2^-23, ceil(|v| * 2^23) * 2^-23, which is the
+//      identity for |v| >= 1 (there the 22 bits below E2M1's mantissa bit are all of f) and
+//      turns f * 2^22 into ceil(f * 2^22) below 1 (grid step 1/2); a value just under a grid
+//      point that rounds up onto it is then rounded up by the converter for every r, as the
+//      rule does. |v| * 2^23 and the products are exact fp32 operations.
 // ---------------------------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t cvt_rne_pack8(const float (&v)[8]) {
   uint32_t w = 0;
@@ -119,19 +123,19 @@ __device__ __forceinline__ uint32_t cvt_rne_pack8(const float (&v)[8]) {
   return w;
 }
 
-// rt[k]: the random field of value k in bits 31..16, zeros below. Each conversion writes its
-// code pair to byte 0, value k in the low nibble; the pair's second value is just the next
-// register (its code is discarded), and the nibble is placed by hand (the compiler does not
-// carry the untouched bytes of the destination through this builtin, so byte selection
-// cannot accumulate a word).
-__device__ __forceinline__ uint32_t cvt_sr_pack8(const float (&v)[8], const uint32_t (&rt)[8]) {
+// The converter writes the pair's codes to byte 0 (the first value in the low nibble); the
+// pair's second value is just the next register, its code is discarded, and the nibble is
+// placed by hand (the compiler does not carry the untouched bytes of the destination through
+// this builtin, so byte selection cannot accumulate a word). rw[k] = (~r_k << 16) | 0xFFFF.
+__device__ __forceinline__ uint32_t sr_pack8(const float (&v)[8], const uint32_t (&rw)[8]) {
   typedef float f32x2_t __attribute__((ext_vector_type(2)));
   uint32_t w = 0;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    const f32x2_t pair = {v[k], v[k < 7 ? k + 1 : k]};
-    const uint32_t b = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, pair, rt[k], 1.0f, 0);
-    w |= (b & 0xFu) << (4 * k);
+    const float up = __builtin_ceilf(fabsf(v[k]) * 8388608.0f) * 1.1920928955078125e-07f;
+    const f32x2_t pair = {__builtin_copysignf(up, v[k]), v[k < 7 ? k + 1 : k]};
+    const uint32_t code = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, pair, rw[k], 1.0f, 0);
+    w |= (code & 0xFu) << (4 * k);
   }
   return w;
 }
@@ -159,16 +163,18 @@ __device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
   return make_uint4(c0, c1, c2, c3);
 }
 
-// Random words for source elements 8g .. 8g+7: field k (16 bits) of the Philox output at
-// counter g, placed in bits 31..16 of rt[k] (field k is the low half of output word k / 2 for
+// Converter random words of source elements 8g .. 8g+7: rw[k] = (~r_k << 16) | 0xFFFF with r_k
+// field k (16 bits) of the Philox output at counter g (the low half of output word k / 2 for
 // even k, the high half for odd k).
-__device__ __forceinline__ void sr_top8(uint64_t g, uint64_t seed, uint32_t (&rt)[8]) {
+__device__ __forceinline__ void sr_rand8(uint64_t g, uint64_t seed, uint32_t (&rw)[8]) {
   const uint4 w = philox4x32_10((uint32_t)g, (uint32_t)(g >> 32), 0u, 0u, (uint32_t)seed,
                                 (uint32_t)(seed >> 32));
-  rt[0] = w.x << 16; rt[1] = w.x & 0xFFFF0000u;
-  rt[2] = w.y << 16; rt[3] = w.y & 0xFFFF0000u;
-  rt[4] = w.z << 16; rt[5] = w.z & 0xFFFF0000u;
-  rt[6] = w.w << 16; rt[7] = w.w & 0xFFFF0000u;
+  const uint32_t nw[4] = {~w.x, ~w.y, ~w.z, ~w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    rw[2 * i] = (nw[i] << 16) | 0xFFFFu;
+    rw[2 * i + 1] = nw[i] | 0xFFFFu;
+  }
 }
 
 // ---------------------------------------------------------------------------------------------

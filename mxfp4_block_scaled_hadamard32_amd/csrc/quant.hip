@@ -102,9 +102,9 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
 #pragma unroll
       for (int k = 0; k < 8; ++k) w[k] = w[k] * inv;
       if (SR) {
-        uint32_t rt[8];
-        sr_top8((uint64_t)g, seed, rt);
-        word = cvt_sr_pack8(w, rt);
+        uint32_t rw[8];
+        sr_rand8((uint64_t)g, seed, rw);
+        word = sr_pack8(w, rw);
       } else {
         word = cvt_rne_pack8(w);
       }
@@ -224,10 +224,10 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
       m = max(m, dpp_u32<kQuadXor2>(m));
       sb[k] = scale_byte<CEIL>(m);
     }
-    uint32_t r[8][8];  // r[j][k]: random word of patch element (j, k)
+    uint32_t r[8][8];  // r[j][k]: converter random word of patch element (j, k)
     if (SR) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) sr_top8((uint64_t)((r0 + j) * cols + c0) >> 3, seed, r[j]);
+      for (int j = 0; j < 8; ++j) sr_rand8((uint64_t)((r0 + j) * cols + c0) >> 3, seed, r[j]);
     }
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -238,10 +238,10 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
 #pragma unroll
         for (int j = 0; j < 8; ++j) col[j] = p[j][k] * inv;
         if (SR) {
-          uint32_t rc[8];
+          uint32_t rc[8];  // column k: element (j, k) of the patch for code j
 #pragma unroll
           for (int j = 0; j < 8; ++j) rc[j] = r[j][k];
-          word = cvt_sr_pack8(col, rc);
+          word = sr_pack8(col, rc);
         } else {
           word = cvt_rne_pack8(col);
         }
@@ -334,9 +334,9 @@ __global__ __launch_bounds__(kThreads) void quant_2d_kernel(
 #pragma unroll
         for (int k = 0; k < 8; ++k) p[j][k] = p[j][k] * inv;
         if (SR) {
-          uint32_t rt[8];
-          sr_top8((uint64_t)((r0 + j) * cols + c0) >> 3, seed, rt);
-          R[j] = cvt_sr_pack8(p[j], rt);
+          uint32_t rw[8];
+          sr_rand8((uint64_t)((r0 + j) * cols + c0) >> 3, seed, rw);
+          R[j] = sr_pack8(p[j], rw);
         } else {
           R[j] = cvt_rne_pack8(p[j]);
         }

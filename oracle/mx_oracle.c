@@ -23,9 +23,7 @@
  *    byte 0xFF and all codes 0.
  *  - Hadamard: unnormalised, natural (Sylvester) order, butterflies of span 1,2,4,8,16 in fp32.
  *  - RNE ties go to the even code; |v| >= 6 saturates.
- *  - SR: dithered truncation on the grid: with frac the exact position of |v| between its two
- *    grid neighbours and u = r16 / 65536, round up iff frac + u >= 1 (checked exactly as
- *    frac * 65536 >= 65536 - r16); r16 is Philox4x32-10 field (i & 7) of counter i >> 3.
+ *  - SR: round up iff r16 < frac * 65536, r16 from Philox4x32-10 field (i & 7) of counter i >> 3.
  *
  * Parity pins: see the tests under tests/ (exhaustive grid/scale checks, SR enumeration,
  * dense Hadamard matrix, transposition invariance). Philox4x32-10 is pinned against an
@@ -164,9 +162,7 @@ int orc_e2m1_encode(float v, int round_mode, uint32_t r16) {
       else if (frac < 0.5f) idx = k;
       else idx = (k % 2 == 0) ? k : k + 1; /* tie: the even code */
     } else {
-      /* floor(position + u) with u = r16 / 2^16: up iff frac + u >= 1. frac * 65536 is exact
-       * (power-of-two scaling) and 65536 - r16 is an integer, so the test is exact. */
-      idx = (frac * 65536.0f >= (float)(65536u - r16)) ? k + 1 : k;
+      idx = ((float)r16 < frac * 65536.0f) ? k + 1 : k;
     }
   }
   return (sign << 3) | idx;

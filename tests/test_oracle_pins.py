@@ -161,12 +161,11 @@ def test_sr_is_unbiased_over_all_random_fields(orc, v):
 
 
 @pytest.mark.parametrize("v", [0.1, 0.3, 0.7, 1.2, 1.6, 2.25, 2.99, 3.3, 4.5, 5.9, -0.9, -5.0,
-                               0.75, 1.0000001, 5.9999995, 0.5, 4.0])
-def test_sr_is_dithered_truncation(orc, v):
-    """SR as dithered truncation, round(x) = grid point floor(t + u) with u uniform on the 2^16
-    field values: over all fields the magnitude rounds up for exactly floor(f 2^16) of them
+                               0.75, 1.0000001, 5.9999995, 0.5, 4.0, 3e-9, 0.7500001])
+def test_sr_up_count_over_all_fields(orc, v):
+    """Over all 2^16 random fields the magnitude rounds up for exactly ceil(f 2^16) of them
     (f the exact position between the grid neighbours, from Fractions), and those are the
-    largest fields, so the decision is monotone in the random draw."""
+    smallest fields: a strict comparison of the field with f 2^16."""
     v32 = float(np.float32(v))
     a = abs(Fraction(v32))
     lo = max(g for g in GRID if g <= a)
@@ -174,8 +173,9 @@ def test_sr_is_dithered_truncation(orc, v):
     f = (a - Fraction(lo)) / (Fraction(hi) - Fraction(lo))
     lo_code = orc.e2m1_encode(float(lo) if v32 >= 0 else -float(lo), 0)
     ups = [r for r in range(1 << 16) if orc.e2m1_encode(v32, 1, r) != lo_code]
-    assert len(ups) == int(f * (1 << 16))  # floor: f * 2^16 >= 0
-    assert ups == list(range((1 << 16) - len(ups), 1 << 16))
+    n = f * (1 << 16)
+    assert len(ups) == (n.numerator + n.denominator - 1) // n.denominator  # ceil
+    assert ups == list(range(len(ups)))
 
 
 def test_sr_unbiased_over_seeds_through_quantizer(orc):
