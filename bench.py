@@ -177,6 +177,39 @@ def load_traffic(launch_flops_key: str):
     return rec.get(launch_flops_key)
 
 
+def fused_epilogue(layer, torch, reps: int = 5):
+    """Outside the timed step: Fprop with its output quantized in the GEMM epilogue (1x32 along N,
+    the layer's quantization options) against Fprop to bf16 followed by the row quantizer."""
+    mx, L = layer.mx, layer
+    had, mask, rule, rnd = L.fprop_q
+    b = L.buf
+    yq = torch.empty((L.T, L.N // 2), dtype=torch.uint8, device="cuda")
+    ys = torch.empty((L.T, L.N // 32), dtype=torch.uint8, device="cuda")
+
+    def fused():
+        mx.mx_gemm_fprop_quant(*b["Xq"], 1, *b["Wq"], 1, alpha_exp=L.alpha["fprop"],
+                               scale_rule=rule, round=rnd, hadamard=had, sign_mask=mask,
+                               seed=L.seeds["X"], codes=yq, scales=ys)
+
+    def separate():
+        mx.mx_gemm_fprop(*b["Xq"], 1, *b["Wq"], 1, alpha_exp=L.alpha["fprop"], out=L.Y)
+        mx.mx_quantize(L.Y, axis=1, scale_rule=rule, round=rnd, hadamard=had, sign_mask=mask,
+                       seed=L.seeds["X"], codes=yq, scales=ys)
+
+    res = {}
+    for name, fn in (("fprop_quant_fused_ms", fused), ("fprop_then_quant_ms", separate)):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = round(e0.elapsed_time(e1) / reps, 4)
+    return res
+
+
 COPY_BYTES = 1 << 30  # the --copy-calibration copy reads and writes 1 GiB
 
 
@@ -325,6 +358,7 @@ def main():
             "traffic": traffic,
         },
     }
+    out["components"].update(fused_epilogue(layer, torch))
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         cb = cpu_baseline(layer, args.cpu_sample_rows)

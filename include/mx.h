@@ -160,6 +160,20 @@ mx_status mx_gemm_wgrad(const uint8_t* dytq, const uint8_t* dyts, int32_t gdy, c
                         const uint8_t* xts, int32_t gx, int64_t N, int64_t K, int64_t T,
                         int32_t alpha_exp, int32_t out_dtype, void* dw, int64_t ldw, void* stream);
 
+/* Fprop with the output quantized in the epilogue [P1 paragraph 1: the Walsh-Hadamard rotation
+ * and stochastic rounding run inside the GEMM epilogue, before the output tile is packed to
+ * 4 bits]. Y = 2^alpha_exp * X . W^T is formed in fp32 exactly as mx_gemm_fprop forms it and,
+ * instead of being stored, quantized as mx_quantize(Y, axis = 1, opts) would quantize that fp32
+ * tensor: 1x32 blocks along N, yq [T][N/2], ys [T][N/32], stochastic-rounding index t * N + n.
+ * Arguments as for mx_gemm_fprop; opts as for mx_quantize. K must be a positive multiple of 128
+ * (MX_ERR_UNSUPPORTED otherwise); yq 4-byte aligned. The fp32 values are not bit-identical to
+ * those of a separate fp32 GEMM with a different accumulation order, so the codes equal the
+ * quantization of some fp32 Y within the GEMM bound of mx_gemm_fprop. */
+mx_status mx_gemm_fprop_quant(const uint8_t* xq, const uint8_t* xs, int32_t gx, const uint8_t* wq,
+                              const uint8_t* ws, int32_t gw, int64_t T, int64_t N, int64_t K,
+                              int32_t alpha_exp, const mx_quant_opts* opts, uint8_t* yq,
+                              uint8_t* ys, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* mx_status_string(int32_t status);
 

@@ -9,6 +9,7 @@ in the library's HIP kernels.
   mx_quantize_2d  32x32 transposition-invariant blocks, plus the transposed K-major copy
   mx_dequantize   codes * 2^(scale-127), optional inverse rotation
   mx_gemm_fprop / mx_gemm_dgrad / mx_gemm_wgrad   block-scaled MXFP4 GEMMs, fp32 accumulate
+  mx_gemm_fprop_quant   Fprop whose output tile is quantized (1x32 along N) in the epilogue
 """
 from __future__ import annotations
 
@@ -21,7 +22,7 @@ from ._lib import (MX_BF16, MX_F32, MX_ROUND_RNE, MX_ROUND_SR, MX_SCALE_CEIL, MX
                    MxError, check, lib, mx_quant_opts)
 
 __all__ = ["mx_quantize", "mx_quantize_2d", "mx_dequantize", "mx_gemm_fprop", "mx_gemm_dgrad",
-           "mx_gemm_wgrad", "MxError", "MX_SCALE_FLOOR", "MX_SCALE_CEIL", "MX_ROUND_RNE",
+           "mx_gemm_wgrad", "mx_gemm_fprop_quant", "MxError", "MX_SCALE_FLOOR", "MX_SCALE_CEIL", "MX_ROUND_RNE",
            "MX_ROUND_SR", "lib"]
 
 
@@ -144,3 +145,23 @@ def mx_gemm_wgrad(dytq, dyts, gdy, xtq, xts, gx, alpha_exp=0, out_dtype=torch.bf
                   stream=None):
     """dW[N][K] = 2^alpha sum_t dYt[n][t] Xt[k][t]; dytq [N][T/2], xtq [K][T/2]."""
     return _gemm("mx_gemm_wgrad", dytq, dyts, gdy, xtq, xts, gx, alpha_exp, out_dtype, out, stream)
+
+
+def mx_gemm_fprop_quant(xq, xs, gx, wq, ws, gw, alpha_exp=0, scale_rule=MX_SCALE_FLOOR,
+                        round=MX_ROUND_RNE, hadamard=0, sign_mask=0, seed=0, codes=None,
+                        scales=None, stream=None):
+    """Y = 2^alpha X W^T in fp32, quantized in the GEMM epilogue along its rows (1x32 blocks
+    along N, options as for mx_quantize) -> (codes [T][N/2], scales [T][N/32])."""
+    T, K = xq.shape[0], 2 * xq.shape[1]
+    N = wq.shape[0]
+    if 2 * wq.shape[1] != K:
+        raise ValueError("operands disagree on the reduction length")
+    if codes is None:
+        codes = torch.empty((T, N // 2), dtype=torch.uint8, device=xq.device)
+    if scales is None:
+        scales = torch.empty((T, N // 32), dtype=torch.uint8, device=xq.device)
+    o = _opts(scale_rule, round, hadamard, sign_mask, seed)
+    check(lib().mx_gemm_fprop_quant(_ptr(xq), _ptr(xs), int(gx), _ptr(wq), _ptr(ws), int(gw), T, N,
+                                    K, int(alpha_exp), ctypes.byref(o), _ptr(codes), _ptr(scales),
+                                    _stream(stream)), "mx_gemm_fprop_quant")
+    return codes, scales

@@ -53,8 +53,10 @@ def lib() -> ctypes.CDLL:
     gemm_args = [vp, vp, i32, vp, vp, i32, i64, i64, i64, i32, i32, vp, i64, vp]
     for name in ("mx_gemm_fprop", "mx_gemm_dgrad", "mx_gemm_wgrad"):
         getattr(L, name).argtypes = gemm_args
+    L.mx_gemm_fprop_quant.argtypes = [vp, vp, i32, vp, vp, i32, i64, i64, i64, i32,
+                                      ctypes.POINTER(mx_quant_opts), vp, vp, vp]
     for name in ("mx_quantize", "mx_quantize_2d", "mx_dequantize", "mx_gemm_fprop",
-                 "mx_gemm_dgrad", "mx_gemm_wgrad"):
+                 "mx_gemm_dgrad", "mx_gemm_wgrad", "mx_gemm_fprop_quant"):
         getattr(L, name).restype = ctypes.c_int
     L.mx_status_string.argtypes = [i32]
     L.mx_status_string.restype = ctypes.c_char_p

@@ -358,12 +358,14 @@ struct StreamCfg {
   }
 };
 
-template <int WAVES, int BKS, int STAGES, int SPLIT3 = 0, int SPLIT0 = 0, int SPLIT1 = 0>
+template <int WAVES, int BKS, int STAGES, int SPLIT3 = 0, int SPLIT0 = 0, int SPLIT1 = 0,
+          bool QOUT = false>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(WAVES / 4, WAVES / 4)))
 void gemm_mx_stream_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, int lga,
                            const uint8_t* __restrict__ B, const uint8_t* __restrict__ Bs, int lgb,
                            int64_t M, int64_t N, int64_t K, float alpha_f, int out_bf16,
-                           void* __restrict__ C, int64_t ldc, int nbm, int nbn) {
+                           void* __restrict__ C, int64_t ldc, int nbm, int nbn,
+                           GemmQuantOut qo) {
   using Cfg = StreamCfg<WAVES, BKS, STAGES>;
   static_assert(WAVES == 4 || WAVES == 8, "4 or 8 waves");
   static_assert((BKS == 2 && STAGES == 4) || (BKS == 4 && STAGES == 2), "stage shapes");
@@ -725,6 +727,67 @@ void gemm_mx_stream_kernel(const uint8_t* __restrict__ A, const uint8_t* __restr
   // instruction touches spread over all banks.
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
+  if constexpr (QOUT) {
+    // Quantized output [P1 paragraph 1: rotate, scale, round and pack the output tile before
+    // it is stored]: the fp32 tile (times 2^alpha) goes to LDS in two halves of 128 rows;
+    // then every quad of lanes takes one 32-column block of a row, as the row quantizer does.
+    constexpr int kPitch = kBN * 4 + 16;
+    constexpr int kPassRows = kBM / 2;
+    static_assert(kPassRows * kPitch <= Cfg::kLds, "fp32 half tile fits in LDS");
+    const int q = t & 3;
+    const int mode = (qo.hadamard ? 1 : 0) | (qo.sr ? 2 : 0) | (qo.ceil ? 4 : 0);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      if ((wm * 32 * FA) / kPassRows == p) {
+#pragma unroll
+        for (int i = 0; i < FA; ++i)
+#pragma unroll
+          for (int j = 0; j < FB; ++j)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+              const int r = wm * 32 * FA + 32 * i + frow - p * kPassRows;
+              const int c = wn * 32 * FB + 32 * j + 8 * rq + 4 * fhalf;
+              *reinterpret_cast<f32x4*>(smem + r * kPitch + 4 * c) =
+                  f32x4{acc[i][j][4 * rq + 0] * alpha_f, acc[i][j][4 * rq + 1] * alpha_f,
+                        acc[i][j][4 * rq + 2] * alpha_f, acc[i][j][4 * rq + 3] * alpha_f};
+            }
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_s_barrier();
+      // round rnd: block b = 64 rnd + t / 4 of the half (row b / 8, 32-column block b % 8)
+      constexpr int kRounds = kPassRows * (kBN / 32) / (64 * WAVES / 4);
+#pragma unroll 1
+      for (int rnd = 0; rnd < kRounds; ++rnd) {
+        const int b = rnd * (16 * WAVES) + (t >> 2);
+        const int r = b >> 3, bc = b & 7;
+        const int64_t m = m0 + p * kPassRows + r, nb = n0 + 32 * bc;
+        if (m >= M || nb >= N) continue;  // whole quads leave together
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(smem + r * kPitch + 4 * (32 * bc + 8 * q));
+        const f32x4 hi = *reinterpret_cast<const f32x4*>(smem + r * kPitch + 4 * (32 * bc + 8 * q) + 16);
+        float w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        const int64_t e0 = m * N + nb + 8 * q;  // row-major index of value 0 in C
+        const uint64_t g = (uint64_t)e0 >> 3;
+        uint32_t sb = 0, word = 0;
+        switch (mode) {
+          case 0: word = mxd::quant_chunk8<false, false, false>(w, q, qo.sign_mask, qo.seed, g, sb); break;
+          case 1: word = mxd::quant_chunk8<true, false, false>(w, q, qo.sign_mask, qo.seed, g, sb); break;
+          case 2: word = mxd::quant_chunk8<false, true, false>(w, q, qo.sign_mask, qo.seed, g, sb); break;
+          case 3: word = mxd::quant_chunk8<true, true, false>(w, q, qo.sign_mask, qo.seed, g, sb); break;
+          case 4: word = mxd::quant_chunk8<false, false, true>(w, q, qo.sign_mask, qo.seed, g, sb); break;
+          case 5: word = mxd::quant_chunk8<true, false, true>(w, q, qo.sign_mask, qo.seed, g, sb); break;
+          case 6: word = mxd::quant_chunk8<false, true, true>(w, q, qo.sign_mask, qo.seed, g, sb); break;
+          default: word = mxd::quant_chunk8<true, true, true>(w, q, qo.sign_mask, qo.seed, g, sb); break;
+        }
+        *reinterpret_cast<uint32_t*>(qo.codes + e0 / 2) = word;
+        if (q == 0) qo.scales[m * (N / 32) + nb / 32] = (uint8_t)sb;
+      }
+      if (p == 0) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_s_barrier();
+      }
+    }
+    return;
+  }
   const bool full = m0 + kBM <= M && n0 + kBN <= N;
   if (out_bf16) {
     constexpr int kPitch = kBN * 2 + 16;
@@ -815,15 +878,36 @@ hipError_t mx_launch_gemm(const GemmArgs& g) {
     hipLaunchKernelGGL((gemm_mx_stream_kernel<kStreamWaves, 4, 2, kS3, kS0, kS1>), grid,
                        dim3(64 * kStreamWaves), 0, (hipStream_t)g.stream, g.a,
                        g.as, lga, g.b, g.bs, lgb, g.M, g.N, g.K, alpha_f, g.out_bf16 ? 1 : 0, g.c,
-                       g.ldc, (int)nbm, (int)nbn);
+                       g.ldc, (int)nbm, (int)nbn, GemmQuantOut{});
   else if (g.K % kBK == 0 && g.K > 0)
     hipLaunchKernelGGL((gemm_mx_stream_kernel<kStreamWaves, 2, 4>), grid, dim3(64 * kStreamWaves), 0,
                        (hipStream_t)g.stream, g.a,
                        g.as, lga, g.b, g.bs, lgb, g.M, g.N, g.K, alpha_f, g.out_bf16 ? 1 : 0, g.c,
-                       g.ldc, (int)nbm, (int)nbn);
+                       g.ldc, (int)nbm, (int)nbn, GemmQuantOut{});
   else
     hipLaunchKernelGGL(gemm_mx_generic_kernel<false>, grid, dim3(kThreads), 0, (hipStream_t)g.stream, g.a,
                        g.as, lga, g.b, g.bs, lgb, g.M, g.N, g.K, alpha_f, g.out_bf16 ? 1 : 0, g.c,
                        g.ldc, (int)nbm, (int)nbn);
+  return hipGetLastError();
+}
+
+hipError_t mx_launch_gemm_quant(const GemmArgs& g, const GemmQuantOut& q) {
+  const int64_t nbm = (g.M + kBM - 1) / kBM, nbn = (g.N + kBN - 1) / kBN;
+  if (nbm * nbn > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if ((int64_t)kBM * (g.K / 2) >= (int64_t)1 << 31) return hipErrorInvalidValue;
+  if (g.K <= 0 || g.K % kBK != 0) return hipErrorInvalidValue;
+  const float alpha_f = __builtin_bit_cast(float, (uint32_t)(g.alpha + 127) << 23);
+  const int lga = g.ga == 32 ? 5 : 0, lgb = g.gb == 32 ? 5 : 0;
+  const dim3 grid((unsigned)(nbm * nbn));
+  constexpr int kS3 = kStreamWaves == 4 ? 8 : 4, kS0 = kStreamWaves == 4 ? 8 : 4;
+  constexpr int kS1 = kStreamWaves == 4 ? 1 : 2;
+  if (g.K % 512 == 0)
+    hipLaunchKernelGGL((gemm_mx_stream_kernel<kStreamWaves, 4, 2, kS3, kS0, kS1, true>), grid,
+                       dim3(64 * kStreamWaves), 0, (hipStream_t)g.stream, g.a, g.as, lga, g.b,
+                       g.bs, lgb, g.M, g.N, g.K, alpha_f, 0, nullptr, 0, (int)nbm, (int)nbn, q);
+  else
+    hipLaunchKernelGGL((gemm_mx_stream_kernel<kStreamWaves, 2, 4, 0, 0, 0, true>), grid,
+                       dim3(64 * kStreamWaves), 0, (hipStream_t)g.stream, g.a, g.as, lga, g.b,
+                       g.bs, lgb, g.M, g.N, g.K, alpha_f, 0, nullptr, 0, (int)nbm, (int)nbn, q);
   return hipGetLastError();
 }

@@ -105,6 +105,26 @@ mx_status mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t row
                                             sign_mask, out, stream));
 }
 
+mx_status mx_gemm_fprop_quant(const uint8_t* xq, const uint8_t* xs, int32_t gx, const uint8_t* wq,
+                              const uint8_t* ws, int32_t gw, int64_t T, int64_t N, int64_t K,
+                              int32_t alpha_exp, const mx_quant_opts* opts, uint8_t* yq,
+                              uint8_t* ys, void* stream) {
+  mx_status s = check_opts(opts);
+  if (s != MX_OK) return s;
+  if (T < 0 || N < 0 || K < 0) return MX_ERR_SHAPE;
+  if (T % 32 || N % 32 || K % 32) return MX_ERR_SHAPE;
+  if ((gx != 1 && gx != 32) || (gw != 1 && gw != 32)) return MX_ERR_ARG;
+  if (alpha_exp < -126 || alpha_exp > 127) return MX_ERR_ARG;
+  if (T == 0 || N == 0) return MX_OK;
+  if (K == 0 || K % 128 != 0) return MX_ERR_UNSUPPORTED;  // the streaming kernels only
+  if (!xq || !xs || !wq || !ws || !yq || !ys) return MX_ERR_NULL;
+  if (!aligned(xq, 16) || !aligned(wq, 16) || !aligned(yq, 4)) return MX_ERR_ARG;
+  GemmArgs g{xq, xs, gx, wq, ws, gw, T, N, K, alpha_exp, false, nullptr, N, stream};
+  GemmQuantOut q{yq, ys, opts->hadamard == 1, opts->round == MX_ROUND_SR,
+                 opts->scale_rule == MX_SCALE_CEIL, opts->sign_mask, opts->seed};
+  return launch_status(mx_launch_gemm_quant(g, q));
+}
+
 mx_status mx_gemm_fprop(const uint8_t* xq, const uint8_t* xs, int32_t gx, const uint8_t* wq,
                         const uint8_t* ws, int32_t gw, int64_t T, int64_t N, int64_t K,
                         int32_t alpha_exp, int32_t out_dtype, void* y, int64_t ldy, void* stream) {

@@ -177,6 +177,49 @@ __device__ __forceinline__ void sr_rand8(uint64_t g, uint64_t seed, uint32_t (&r
   }
 }
 
+__device__ __forceinline__ uint32_t abs_bits(float v) { return __float_as_uint(v) & 0x7FFFFFFFu; }
+
+// ---------------------------------------------------------------------------------------------
+// One lane's 8 values of a 1x32 block, the block held by the 4 lanes of a DPP quad (lane q
+// holds positions 8q .. 8q+7), in the order the pages give [P1 paragraph 2; P3 "Why FP4 ..."]:
+// random signs and the Hadamard transform (HAD), block maximum, scale byte, v = x * 2^-e,
+// rounding, packing. g is the chunk's index for the random fields (source element index of
+// value 0, divided by 8). Returns the 8 codes (value k in nibble k); sb gets the block's scale
+// byte, equal on the 4 lanes. All 4 lanes of the quad must be active.
+// ---------------------------------------------------------------------------------------------
+template <bool HAD, bool SR, bool CEIL>
+__device__ __forceinline__ uint32_t quant_chunk8(float (&w)[8], int q, uint32_t sign_mask,
+                                                 uint64_t seed, uint64_t g, uint32_t& sb) {
+  if (HAD) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      w[k] = __uint_as_float(__float_as_uint(w[k]) ^ (((sign_mask >> (8 * q + k)) & 1u) << 31));
+    fwht8_inlane(w);
+    const uint32_t up8 = (q & 1) ? 0x80000000u : 0u;
+    const uint32_t up16 = (q & 2) ? 0x80000000u : 0u;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) w[k] = butterfly_xlane<kQuadXor1>(w[k], up8);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) w[k] = butterfly_xlane<kQuadXor2>(w[k], up16);
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) m = max(m, abs_bits(w[k]));
+  m = max(m, dpp_u32<kQuadXor1>(m));
+  m = max(m, dpp_u32<kQuadXor2>(m));
+  sb = scale_byte<CEIL>(m);
+  if (sb == 0xFFu) return 0u;
+  const float inv = inv_scale_from_byte(sb);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) w[k] = w[k] * inv;
+  if (SR) {
+    uint32_t rw[8];
+    sr_rand8(g, seed, rw);
+    return sr_pack8(w, rw);
+  }
+  return cvt_rne_pack8(w);
+}
+
 // ---------------------------------------------------------------------------------------------
 // in-lane transpose of an 8x8 matrix of nibbles: R[j] nibble k -> R[k] nibble j
 // (swap 4x4 quadrants, then 2x2 sub-blocks, then single nibbles)

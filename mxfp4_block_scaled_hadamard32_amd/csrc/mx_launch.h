@@ -44,3 +44,16 @@ struct GemmArgs {
 };
 
 hipError_t mx_launch_gemm(const GemmArgs& g);
+
+// Epilogue quantization of C along its rows (1x32 blocks along N), instead of storing C:
+// codes [M][N/2], scales [M][N/32]; the random-field index of C[m][n] is m * N + n.
+struct GemmQuantOut {
+  uint8_t* codes;
+  uint8_t* scales;
+  bool hadamard, sr, ceil;
+  uint32_t sign_mask;
+  uint64_t seed;
+};
+
+// K must be a multiple of 128 (the streaming kernels); returns hipErrorInvalidValue otherwise.
+hipError_t mx_launch_gemm_quant(const GemmArgs& g, const GemmQuantOut& q);

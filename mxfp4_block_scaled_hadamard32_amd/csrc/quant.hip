@@ -45,8 +45,6 @@ __device__ __forceinline__ void load8(const void* __restrict__ x, int64_t off, f
   }
 }
 
-__device__ __forceinline__ uint32_t abs_bits(float v) { return __float_as_uint(v) & 0x7FFFFFFFu; }
-
 // ---------------------------------------------------------------------------------------------
 // 1x32 blocks along rows. Chunk g = 8 consecutive elements, row-major over the logical tensor,
 // so element index 8g + k is also the stochastic-rounding index.
@@ -56,11 +54,6 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
     const void* __restrict__ x, int64_t nchunks, int64_t cpr, int64_t ld, int contiguous,
     uint32_t sign_mask, uint64_t seed, uint32_t* __restrict__ codes, uint8_t* __restrict__ scales) {
   const int q = threadIdx.x & 3;
-  uint32_t sgn[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) sgn[k] = HAD ? (((sign_mask >> (8 * q + k)) & 1u) << 31) : 0u;
-  const uint32_t up8 = (q & 1) ? 0x80000000u : 0u;
-  const uint32_t up16 = (q & 2) ? 0x80000000u : 0u;
 
   const int64_t base = (int64_t)blockIdx.x * (kThreads * kRowChunksPerThread) + threadIdx.x;
   float v[kRowChunksPerThread][8];
@@ -80,35 +73,8 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
   for (int u = 0; u < kRowChunksPerThread; ++u) {
     const int64_t g = base + (int64_t)u * kThreads;
     if (g >= nchunks) continue;  // quads are all in or all out (cols % 32 == 0)
-    float (&w)[8] = v[u];
-    if (HAD) {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) w[k] = __uint_as_float(__float_as_uint(w[k]) ^ sgn[k]);
-      fwht8_inlane(w);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) w[k] = butterfly_xlane<kQuadXor1>(w[k], up8);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) w[k] = butterfly_xlane<kQuadXor2>(w[k], up16);
-    }
-    uint32_t m = 0;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) m = max(m, abs_bits(w[k]));
-    m = max(m, dpp_u32<kQuadXor1>(m));
-    m = max(m, dpp_u32<kQuadXor2>(m));
-    const uint32_t sb = scale_byte<CEIL>(m);
-    uint32_t word = 0;
-    if (sb != 0xFFu) {
-      const float inv = inv_scale_from_byte(sb);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) w[k] = w[k] * inv;
-      if (SR) {
-        uint32_t rw[8];
-        sr_rand8((uint64_t)g, seed, rw);
-        word = sr_pack8(w, rw);
-      } else {
-        word = cvt_rne_pack8(w);
-      }
-    }
+    uint32_t sb;
+    const uint32_t word = quant_chunk8<HAD, SR, CEIL>(v[u], q, sign_mask, seed, (uint64_t)g, sb);
     __builtin_nontemporal_store(word, codes + g);
     if (q == 0) scales[g >> 2] = (uint8_t)sb;
   }
