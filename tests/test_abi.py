@@ -108,3 +108,23 @@ def test_gemm_argument_errors(L, name):
     assert call(a=None) == m.MX_ERR_NULL
     assert call(M=0) == m.MX_OK and call(N=0, c=None) == m.MX_OK
     del ok
+
+
+def test_gemm_fprop_quant_argument_errors(L):
+    from mxfp4_block_scaled_hadamard32_amd import _lib as m
+    g = L.mx_gemm_fprop_quant
+
+    def call(T=64, N=64, K=128, gx=1, gw=1, alpha=0, o=None, yq=FAKE, ys=FAKE, xq=FAKE):
+        return g(xq, FAKE, gx, FAKE, FAKE, gw, T, N, K, alpha, opts() if o is None else o, yq, ys,
+                 None)
+    assert call(T=48) == m.MX_ERR_SHAPE
+    assert call(K=40) == m.MX_ERR_SHAPE
+    assert call(K=96) == m.MX_ERR_UNSUPPORTED   # the epilogue runs in the 128-k streaming kernels
+    assert call(gx=2) == m.MX_ERR_ARG
+    assert call(alpha=-200) == m.MX_ERR_ARG
+    assert call(o=opts(scale_rule=3)) == m.MX_ERR_ARG
+    assert g(FAKE, FAKE, 1, FAKE, FAKE, 1, 64, 64, 128, 0, None, FAKE, FAKE, None) == m.MX_ERR_NULL
+    assert call(ys=None) == m.MX_ERR_NULL
+    assert call(xq=None) == m.MX_ERR_NULL
+    assert call(yq=ctypes.c_void_p(0x10002)) == m.MX_ERR_ARG
+    assert call(T=0, yq=None, ys=None) == m.MX_OK
