@@ -18,6 +18,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -49,6 +50,9 @@ def parse():
                    help="source rows per operand quantization in the CPU oracle sample")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also launch one plain 1 GiB device copy (counter calibration runs)")
+    p.add_argument("--step-only", action="store_true",
+                   help="skip the comparisons run after the timed steps (fused epilogue, linear "
+                        "layer), so that a profile of the run holds the step's launches alone")
     p.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="no GPU work: turn the counter_collection.csv files of a FETCH_SIZE and "
                         "a WRITE_SIZE rocprofv3 pass over a --copy-calibration run into the "
@@ -210,6 +214,42 @@ def fused_epilogue(layer, torch, reps: int = 5):
     return res
 
 
+def linear_layer(layer, torch, reps: int = 3):
+    """Outside the timed step: forward + backward of the MXFP4 linear layer (autograd op, the
+    layer's quantization options on all three GEMMs) against the same op with every GEMM in bf16."""
+    from mxfp4_block_scaled_hadamard32_amd import linear
+    L = layer
+
+    def spec(q):
+        had, mask, rule, rnd = q
+        return linear.QuantSpec(scale_rule=rule, round=rnd, hadamard=had, sign_mask=mask)
+
+    x = L.X.detach().requires_grad_(True)
+    w = L.W.detach().requires_grad_(True)
+    dy = L.dY
+    res = {}
+    for name, cfg in (
+            ("mx_linear_fwd_bwd_ms", linear.MXLinearConfig(fprop_q=spec(L.fprop_q),
+                                                            dgrad_q=spec(L.dgrad_q),
+                                                            wgrad_q=spec(L.wgrad_q))),
+            ("bf16_linear_fwd_bwd_ms", linear.MXLinearConfig(fprop=False, dgrad=False,
+                                                              wgrad=False))):
+        def run():
+            x.grad = w.grad = None
+            linear.MXLinearFunction.apply(x, w, cfg).backward(dy)
+        run()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = round(e0.elapsed_time(e1) / reps, 4)
+    x.grad = w.grad = None
+    return res
+
+
 COPY_BYTES = 1 << 30  # the --copy-calibration copy reads and writes 1 GiB
 
 
@@ -251,7 +291,9 @@ def write_traffic(fetch_csv: str, write_csv: str, workload: str):
     wf = COPY_BYTES / (copy_value(write) * 1024.0)
 
     def gemm_value(table, wgs):
-        vals = [vs for (name, g), vs in table.items() if "gemm_mx" in name and g == wgs]
+        # the plain-output GEMM (last template argument false), not the quantizing epilogue
+        vals = [vs for (name, g), vs in table.items()
+                if re.search(r"gemm_mx\w*<[^>]*false>", name) and g == wgs]
         if len(vals) != 1:
             raise SystemExit(f"expected one GEMM kernel with {wgs} workgroups, found {len(vals)}")
         return sum(vals[0]) / len(vals[0])
@@ -259,10 +301,10 @@ def write_traffic(fetch_csv: str, write_csv: str, workload: str):
     rec = {"gemm_sha": sha(GEMM_SRC), "fetch_factor": ff, "write_factor": wf,
            "command_fetch": ("rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch "
                              "-o run -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline "
-                             "--copy-calibration"),
+                             "--step-only --copy-calibration"),
            "command_write": ("rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write "
                              "-o run -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline "
-                             "--copy-calibration")}
+                             "--step-only --copy-calibration")}
     for name, M, Nn, Kk in (("fprop", T, N, K), ("dgrad", T, K, N), ("wgrad", N, K, T)):
         wgs = ((M + 255) // 256) * ((Nn + 255) // 256)
         hbm = gemm_value(fetch, wgs) * 1024.0 * ff + gemm_value(write, wgs) * 1024.0 * wf
@@ -358,7 +400,9 @@ def main():
             "traffic": traffic,
         },
     }
-    out["components"].update(fused_epilogue(layer, torch))
+    if not args.step_only:
+        out["components"].update(fused_epilogue(layer, torch))
+        out["components"].update(linear_layer(layer, torch))
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         cb = cpu_baseline(layer, args.cpu_sample_rows)
