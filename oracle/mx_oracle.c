@@ -24,6 +24,9 @@
  *  - Hadamard: unnormalised, natural (Sylvester) order, butterflies of span 1,2,4,8,16 in fp32.
  *  - RNE ties go to the even code; |v| >= 6 saturates.
  *  - SR: round up iff r16 < frac * 65536, r16 from Philox4x32-10 field (i & 7) of counter i >> 3.
+ *  - MXFP8 (E4M3 / E5M2 elements): OCP MX FP8 element encodings; floor scale e =
+ *    floor(log2 amax) - emax (8 or 15), ceil scale the least e with amax <= largest * 2^e;
+ *    |v| >= largest saturates; rounding and the random fields as for E2M1.
  *
  * Parity pins: see the tests under tests/ (exhaustive grid/scale checks, SR enumeration,
  * dense Hadamard matrix, transposition invariance). Philox4x32-10 is pinned against an
@@ -319,6 +322,163 @@ int orc_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, in
         }
       }
     }
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* MXFP8 [P3 "The fix, and its supporting cast": queries and keys are quantized in MXFP8]:    */
+/* the same E8M0 scale per 32 consecutive values, with 8-bit E4M3 (fmt 0) or E5M2 (fmt 1)     */
+/* elements. The pages fix neither encoding; both are the OCP MX FP8 element types (reading): */
+/*   E4M3: 4 exponent bits (bias 7), 3 mantissa bits; exponent 15 with mantissa 7 is NaN, no  */
+/*         infinity, so the largest magnitude is 1.75 * 2^8 = 448.                            */
+/*   E5M2: 5 exponent bits (bias 15), 2 mantissa bits; exponent 31 is inf / NaN, so the        */
+/*         largest magnitude is 1.75 * 2^15 = 57344.                                          */
+/* Exponent field 0 is subnormal: M * 2^(1 - bias - mbits). Codes 0..max_code of the 7-bit   */
+/* magnitude are finite and increase with the code.                                          */
+/* ------------------------------------------------------------------------------------------ */
+static void fp8_fields(int fmt, int* ebits, int* mbits, int* bias, int* max_code) {
+  if (fmt == 0) {
+    *ebits = 4; *mbits = 3; *bias = 7; *max_code = 0x7E;
+  } else {
+    *ebits = 5; *mbits = 2; *bias = 15; *max_code = 0x7B;
+  }
+}
+
+/* magnitude of 7-bit code m; inf or NaN for the non-finite codes */
+double orc_fp8_magnitude(int m, int fmt) {
+  int ebits, mbits, bias, max_code;
+  fp8_fields(fmt, &ebits, &mbits, &bias, &max_code);
+  m &= 0x7F;
+  int E = m >> mbits, M = m & ((1 << mbits) - 1);
+  if (m > max_code) {
+    if (fmt == 1 && M == 0) return INFINITY;
+    return NAN;
+  }
+  if (E == 0) return ldexp((double)M, 1 - bias - mbits);
+  return ldexp(1.0 + ldexp((double)M, -mbits), E - bias);
+}
+
+double orc_fp8_decode(int code, int fmt) {
+  double mag = orc_fp8_magnitude(code & 0x7F, fmt);
+  return (code & 0x80) ? -mag : mag;
+}
+
+/* Scale exponent: floor (OCP) e = floor(log2 amax) - emax with emax the exponent of the      */
+/* largest magnitude (8 or 15); ceil: the least e with amax <= largest * 2^e, found by        */
+/* stepping up from the floor value (exact in double). Clamped to [-127, 127]; amax = 0 ->    */
+/* -127. amax must be finite.                                                                 */
+int orc_fp8_scale_exponent(float amax, int scale_rule, int fmt) {
+  int ebits, mbits, bias, max_code;
+  fp8_fields(fmt, &ebits, &mbits, &bias, &max_code);
+  if (amax == 0.0f) return -127;
+  const double largest = orc_fp8_magnitude(max_code, fmt);
+  const int emax = (max_code >> mbits) - bias;
+  int E2;
+  frexpf(amax, &E2); /* amax in [2^(E2-1), 2^E2) */
+  int e = (E2 - 1) - emax;
+  if (scale_rule == 1)
+    while (ldexp(largest, e) < (double)amax) ++e;
+  if (e < -127) e = -127;
+  if (e > 127) e = 127;
+  return e;
+}
+
+/* Rounding of a scaled value v to the format: |v| >= largest saturates; otherwise lo <= |v| < */
+/* hi are the neighbouring magnitudes, frac = (|v| - lo) / (hi - lo) is exact in fp32 (lo >=   */
+/* |v|/2 or a multiple of the subnormal step; hi - lo is a power of two). Nearest with ties to */
+/* the even code, or stochastic: up iff r16 < frac * 65536. The sign is copied (bit 7).       */
+int orc_fp8_encode(float v, int fmt, int round_mode, uint32_t r16) {
+  int ebits, mbits, bias, max_code;
+  fp8_fields(fmt, &ebits, &mbits, &bias, &max_code);
+  int sign = signbit(v) ? 1 : 0;
+  float a = fabsf(v);
+  int idx;
+  if ((double)a >= orc_fp8_magnitude(max_code, fmt)) {
+    idx = max_code;
+  } else {
+    /* largest code k with magnitude(k) <= a, by bisection over the increasing magnitudes */
+    int k = 0, top = max_code; /* invariant: magnitude(k) <= a < magnitude(top) */
+    while (top - k > 1) {
+      int mid = (k + top) / 2;
+      if (orc_fp8_magnitude(mid, fmt) <= (double)a) k = mid;
+      else top = mid;
+    }
+    float lo = (float)orc_fp8_magnitude(k, fmt);
+    float hi = (float)orc_fp8_magnitude(k + 1, fmt);
+    float frac = (a - lo) / (hi - lo);
+    if (round_mode == 0) {
+      if (frac > 0.5f) idx = k + 1;
+      else if (frac < 0.5f) idx = k;
+      else idx = (k % 2 == 0) ? k : k + 1;
+    } else {
+      idx = ((float)r16 < frac * 65536.0f) ? k + 1 : k;
+    }
+  }
+  return (sign << 7) | idx;
+}
+
+/* One 32-value block in the order of the FP4 path: signs and transform (optional), block     */
+/* maximum, scale, v = x * 2^-e, rounding. Non-finite block: byte 0xFF, codes 0.              */
+static uint8_t quantize_block_fp8(float* vals, const uint64_t* idx, int fmt, const orc_opts* o,
+                                  int* codes) {
+  if (o->hadamard) {
+    for (int j = 0; j < 32; ++j)
+      if ((o->sign_mask >> j) & 1u) vals[j] = -vals[j];
+    orc_fwht32(vals);
+  }
+  float amax = 0.0f;
+  int finite = 1;
+  for (int j = 0; j < 32; ++j) {
+    float a = fabsf(vals[j]);
+    if (!isfinite(a)) finite = 0;
+    if (a > amax) amax = a;
+  }
+  if (!finite) {
+    for (int j = 0; j < 32; ++j) codes[j] = 0;
+    return 0xFF;
+  }
+  int e = orc_fp8_scale_exponent(amax, o->scale_rule, fmt);
+  float inv_scale = ldexpf(1.0f, -e);
+  for (int j = 0; j < 32; ++j) {
+    float v = vals[j] * inv_scale;
+    uint32_t r16 = o->round ? orc_sr_field(o->seed, idx[j]) : 0u;
+    codes[j] = orc_fp8_encode(v, fmt, o->round, r16);
+  }
+  return (uint8_t)(e + 127);
+}
+
+/* 1x32 MXFP8 quantize, one code byte per element, rows [row_begin, row_end):                */
+/*   axis 1: codes[rows][cols], scales[rows][cols/32]                                         */
+/*   axis 0: codes[cols][rows], scales[cols][rows/32]  (layout of the transpose)              */
+int orc_quantize_fp8(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int axis,
+                     int fmt, const orc_opts* o, uint8_t* codes, uint8_t* scales,
+                     int64_t row_begin, int64_t row_end) {
+  float vals[32];
+  uint64_t idx[32];
+  int cds[32];
+  if (axis == 1) {
+    for (int64_t r = row_begin; r < row_end; ++r)
+      for (int64_t b = 0; b < cols / 32; ++b) {
+        for (int j = 0; j < 32; ++j) {
+          int64_t c = b * 32 + j;
+          vals[j] = widen(x, dtype, r * ld + c);
+          idx[j] = (uint64_t)(r * cols + c);
+        }
+        scales[r * (cols / 32) + b] = quantize_block_fp8(vals, idx, fmt, o, cds);
+        for (int j = 0; j < 32; ++j) codes[r * cols + b * 32 + j] = (uint8_t)cds[j];
+      }
+  } else {
+    for (int64_t b = row_begin / 32; b < row_end / 32; ++b)
+      for (int64_t c = 0; c < cols; ++c) {
+        for (int j = 0; j < 32; ++j) {
+          int64_t r = b * 32 + j;
+          vals[j] = widen(x, dtype, r * ld + c);
+          idx[j] = (uint64_t)(r * cols + c);
+        }
+        scales[c * (rows / 32) + b] = quantize_block_fp8(vals, idx, fmt, o, cds);
+        for (int j = 0; j < 32; ++j) codes[c * rows + b * 32 + j] = (uint8_t)cds[j];
+      }
   }
   return 0;
 }

@@ -32,6 +32,7 @@ LIB_PATH = os.path.join(HERE, "liboracle.so")
 
 SCALE_FLOOR, SCALE_CEIL = 0, 1
 ROUND_RNE, ROUND_SR = 0, 1
+E4M3, E5M2 = 0, 1
 
 
 class _Opts(ctypes.Structure):
@@ -70,6 +71,16 @@ def lib():
         L.orc_e2m1_decode.restype = ctypes.c_float
         L.orc_e2m1_magnitude.argtypes = [i32]
         L.orc_e2m1_magnitude.restype = ctypes.c_float
+        L.orc_fp8_magnitude.argtypes = [i32, i32]
+        L.orc_fp8_magnitude.restype = ctypes.c_double
+        L.orc_fp8_decode.argtypes = [i32, i32]
+        L.orc_fp8_decode.restype = ctypes.c_double
+        L.orc_fp8_scale_exponent.argtypes = [ctypes.c_float, i32, i32]
+        L.orc_fp8_scale_exponent.restype = ctypes.c_int
+        L.orc_fp8_encode.argtypes = [ctypes.c_float, i32, i32, ctypes.c_uint32]
+        L.orc_fp8_encode.restype = ctypes.c_int
+        L.orc_quantize_fp8.argtypes = [vp, i32, i64, i64, i64, i32, i32, ctypes.POINTER(_Opts),
+                                       vp, vp, i64, i64]
         _lib = L
     return _lib
 
@@ -136,6 +147,22 @@ def fwht32(x) -> np.ndarray:
     return y
 
 
+def fp8_magnitude(m: int, fmt: int) -> float:
+    return float(lib().orc_fp8_magnitude(int(m), int(fmt)))
+
+
+def fp8_decode(code: int, fmt: int) -> float:
+    return float(lib().orc_fp8_decode(int(code), int(fmt)))
+
+
+def fp8_encode(v: float, fmt: int, round_mode: int = ROUND_RNE, r16: int = 0) -> int:
+    return int(lib().orc_fp8_encode(ctypes.c_float(v), int(fmt), int(round_mode), int(r16)))
+
+
+def fp8_scale_exponent(amax: float, scale_rule: int, fmt: int) -> int:
+    return int(lib().orc_fp8_scale_exponent(ctypes.c_float(amax), int(scale_rule), int(fmt)))
+
+
 # ----------------------------------------------------------------------------------------------
 # tensor quantizers
 # ----------------------------------------------------------------------------------------------
@@ -198,6 +225,28 @@ def dequantize(codes: np.ndarray, scales: np.ndarray, rows: int, cols: int, bloc
     return out
 
 
+def quantize_fp8(x: np.ndarray, fmt: int = E4M3, axis: int = 1, scale_rule: int = SCALE_FLOOR,
+                 round_mode: int = ROUND_RNE, hadamard: int = 0, sign_mask: int = 0,
+                 seed: int = 0, row_range=None):
+    """1x32 MXFP8 quantize, one code byte per element. axis=1: codes [rows][cols], scales
+    [rows][cols/32]; axis=0: codes [cols][rows], scales [cols][rows/32]."""
+    dt, ld = _src(x)
+    rows, cols = x.shape
+    if (cols if axis == 1 else rows) % 32:
+        raise ValueError("the blocked dimension must be a multiple of 32")
+    if axis == 1:
+        codes = np.zeros((rows, cols), dtype=np.uint8)
+        scales = np.zeros((rows, cols // 32), dtype=np.uint8)
+    else:
+        codes = np.zeros((cols, rows), dtype=np.uint8)
+        scales = np.zeros((cols, rows // 32), dtype=np.uint8)
+    r0, r1 = (0, rows) if row_range is None else row_range
+    o = _opts(scale_rule, round_mode, hadamard, sign_mask, seed)
+    lib().orc_quantize_fp8(_ptr(x), dt, rows, cols, ld, axis, int(fmt), ctypes.byref(o),
+                           _ptr(codes), _ptr(scales), r0, r1)
+    return codes, scales
+
+
 # ----------------------------------------------------------------------------------------------
 # GEMM: plain definition in float64
 # ----------------------------------------------------------------------------------------------
@@ -232,3 +281,28 @@ def gemm(aq, as_, ga: int, bq, bs, gb: int, M: int, N: int, K: int, alpha_exp: i
     C = (A @ B.T) * f
     Cabs = (np.abs(A) @ np.abs(B).T) * f
     return C, Cabs
+
+
+def _fp8_values_f64(fmt: int) -> np.ndarray:
+    return np.array([fp8_decode(c, fmt) for c in range(256)], dtype=np.float64)
+
+
+def dequantize_fp8_f64(codes: np.ndarray, scales: np.ndarray, rows: int, k: int, fmt: int,
+                       row_index=None) -> np.ndarray:
+    """Exact float64 values of a K-major MXFP8 operand: codes [rows][k], scales [rows][k/32]."""
+    codes = np.asarray(codes, dtype=np.uint8).reshape(rows, k)
+    scales = np.asarray(scales, dtype=np.uint8).reshape(rows, k // 32)
+    ridx = np.arange(rows) if row_index is None else np.asarray(row_index)
+    vals = _fp8_values_f64(fmt)[codes[ridx]]
+    s = scales[ridx].astype(np.int64)
+    pw = np.where(s == 255, np.nan, np.ldexp(1.0, s - 127))
+    return vals * np.repeat(pw, 32, axis=1)
+
+
+def gemm_fp8(aq, as_, afmt: int, bq, bs, bfmt: int, M: int, N: int, K: int, alpha_exp: int = 0,
+             rows=None, cols=None):
+    """MXFP8 C[m][n] = 2^alpha * sum_k A[m][k] B[n][k] in float64 and sum |a_k b_k| (as gemm)."""
+    A = dequantize_fp8_f64(aq, as_, M, K, afmt, rows)
+    B = dequantize_fp8_f64(bq, bs, N, K, bfmt, cols)
+    f = 2.0 ** alpha_exp
+    return (A @ B.T) * f, (np.abs(A) @ np.abs(B).T) * f
