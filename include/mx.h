@@ -174,6 +174,42 @@ mx_status mx_gemm_fprop_quant(const uint8_t* xq, const uint8_t* xs, int32_t gx, 
                               int32_t alpha_exp, const mx_quant_opts* opts, uint8_t* yq,
                               uint8_t* ys, void* stream);
 
+/* MXFP8 [P3, "The fix, and its supporting cast": the query and key projections are quantized
+ * in MXFP8 rather than FP4]. Blocks, scales, options and stochastic-rounding fields are those
+ * of the MXFP4 path; the elements are 8-bit OCP floating point (the pages do not fix the
+ * encoding):
+ *  MX_E4M3: sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent 15 with mantissa 7 is
+ *           NaN and there is no infinity, so the largest magnitude is 448 = 1.75 * 2^8;
+ *  MX_E5M2: sign, 5 exponent bits (bias 15), 2 mantissa bits; exponent 31 is inf / NaN, the
+ *           largest magnitude is 57344 = 1.75 * 2^15.
+ * Exponent field 0 is subnormal. A code is one byte, the sign in bit 7 (copied from the value).
+ * Scale exponent, with amax = m * 2^E, m in [1, 2): MX_SCALE_FLOOR e = E - emax (emax = 8 or
+ * 15, the exponent of the largest magnitude; values beyond it saturate); MX_SCALE_CEIL the
+ * least e with amax <= largest * 2^e. MX_ROUND_RNE rounds to the nearest representable value
+ * with ties to the even code; MX_ROUND_SR rounds up iff r < f * 2^16 as for E2M1; |v| >= the
+ * largest magnitude gives the largest code. */
+typedef enum { MX_E4M3 = 0, MX_E5M2 = 1 } mx_fp8_format;
+
+/* 1x32 MXFP8 quantize; arguments as for mx_quantize plus fmt (mx_fp8_format).
+ * axis = 1: codes [rows][cols] (one byte per element), scales [rows][cols/32];
+ * axis = 0: codes [cols][rows], scales [cols][rows/32] (the K-major layout of the transpose).
+ * Alignment: x and source rows 16 bytes; codes 8 bytes (axis = 1) or 16 bytes (axis = 0);
+ * axis = 0 also needs cols % 8 == 0. Errors as for mx_quantize; MX_ERR_ARG for a bad fmt. */
+mx_status mx_quantize_mxfp8(const void* x, int32_t dtype, int64_t rows, int64_t cols, int64_t ld,
+                            int32_t axis, int32_t fmt, const mx_quant_opts* opts, uint8_t* codes,
+                            uint8_t* scales, void* stream);
+
+/* MXFP8 GEMM on gfx950's block-scaled matrix cores: C[m][n] = 2^alpha_exp * sum_k A[m][k] *
+ * B[n][k], fp32 accumulation, with A codes [M][K] of format afmt and B codes [N][K] of format
+ * bfmt (one byte per element, K-major), scales [M][K/32] and [N][K/32]. Fprop, Dgrad and Wgrad
+ * are this call on the operands of the respective orientation (as for the MXFP4 calls).
+ * M, N multiples of 32; K a positive multiple of 128 (MX_ERR_UNSUPPORTED otherwise, except
+ * K == 0, which writes zeros); operand codes and C 16-byte aligned; ldc a multiple of 8
+ * elements; 256 * K < 2^31. out_dtype, alpha_exp and errors as for mx_gemm_fprop. */
+mx_status mx_gemm_mxfp8(const uint8_t* aq, const uint8_t* as, int32_t afmt, const uint8_t* bq,
+                        const uint8_t* bs, int32_t bfmt, int64_t M, int64_t N, int64_t K,
+                        int32_t alpha_exp, int32_t out_dtype, void* c, int64_t ldc, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* mx_status_string(int32_t status);
 

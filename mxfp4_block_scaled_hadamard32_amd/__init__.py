@@ -10,6 +10,8 @@ in the library's HIP kernels.
   mx_dequantize   codes * 2^(scale-127), optional inverse rotation
   mx_gemm_fprop / mx_gemm_dgrad / mx_gemm_wgrad   block-scaled MXFP4 GEMMs, fp32 accumulate
   mx_gemm_fprop_quant   Fprop whose output tile is quantized (1x32 along N) in the epilogue
+  mx_quantize_mxfp8 / mx_gemm_mxfp8   MXFP8 (E4M3 / E5M2 elements, the same E8M0 block scales)
+                  quantize and block-scaled GEMM, for the query / key projections
 """
 from __future__ import annotations
 
@@ -18,12 +20,13 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import (MX_BF16, MX_F32, MX_ROUND_RNE, MX_ROUND_SR, MX_SCALE_CEIL, MX_SCALE_FLOOR,
-                   MxError, check, lib, mx_quant_opts)
+from ._lib import (MX_BF16, MX_E4M3, MX_E5M2, MX_F32, MX_ROUND_RNE, MX_ROUND_SR, MX_SCALE_CEIL,
+                   MX_SCALE_FLOOR, MxError, check, lib, mx_quant_opts)
 
 __all__ = ["mx_quantize", "mx_quantize_2d", "mx_dequantize", "mx_gemm_fprop", "mx_gemm_dgrad",
-           "mx_gemm_wgrad", "mx_gemm_fprop_quant", "MxError", "MX_SCALE_FLOOR", "MX_SCALE_CEIL", "MX_ROUND_RNE",
-           "MX_ROUND_SR", "lib"]
+           "mx_gemm_wgrad", "mx_gemm_fprop_quant", "mx_quantize_mxfp8", "mx_gemm_mxfp8", "MxError",
+           "MX_SCALE_FLOOR", "MX_SCALE_CEIL", "MX_ROUND_RNE", "MX_ROUND_SR", "MX_E4M3", "MX_E5M2",
+           "lib"]
 
 
 def _stream(stream) -> ctypes.c_void_p:
@@ -165,3 +168,39 @@ def mx_gemm_fprop_quant(xq, xs, gx, wq, ws, gw, alpha_exp=0, scale_rule=MX_SCALE
                                     K, int(alpha_exp), ctypes.byref(o), _ptr(codes), _ptr(scales),
                                     _stream(stream)), "mx_gemm_fprop_quant")
     return codes, scales
+
+
+def mx_quantize_mxfp8(x: torch.Tensor, fmt: int = MX_E4M3, axis: int = 1,
+                      scale_rule: int = MX_SCALE_FLOOR, round: int = MX_ROUND_RNE,
+                      hadamard: int = 0, sign_mask: int = 0, seed: int = 0,
+                      codes: torch.Tensor | None = None, scales: torch.Tensor | None = None,
+                      stream=None):
+    """1x32 MXFP8 quantize (fmt MX_E4M3 or MX_E5M2). axis=1 -> codes [rows][cols] (one byte per
+    element), scales [rows][cols/32]; axis=0 -> codes [cols][rows], scales [cols][rows/32]."""
+    rows, cols, ld = _src(x)
+    shape_c = (rows, cols) if axis == 1 else (cols, rows)
+    shape_s = (rows, cols // 32) if axis == 1 else (cols, rows // 32)
+    if codes is None:
+        codes = torch.empty(shape_c, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(shape_s, dtype=torch.uint8, device=x.device)
+    o = _opts(scale_rule, round, hadamard, sign_mask, seed)
+    check(lib().mx_quantize_mxfp8(_ptr(x), _dtype_code(x), rows, cols, ld, int(axis), int(fmt),
+                                  ctypes.byref(o), _ptr(codes), _ptr(scales), _stream(stream)),
+          "mx_quantize_mxfp8")
+    return codes, scales
+
+
+def mx_gemm_mxfp8(aq, as_, afmt, bq, bs, bfmt, alpha_exp=0, out_dtype=torch.bfloat16, out=None,
+                  stream=None):
+    """C[M][N] = 2^alpha sum_k A[m][k] B[n][k]; aq [M][K], bq [N][K] MXFP8 codes of formats
+    afmt / bfmt, scales [M][K/32], [N][K/32]."""
+    M, K = aq.shape
+    N = bq.shape[0]
+    if bq.shape[1] != K:
+        raise ValueError("operands disagree on the reduction length")
+    out, code = _out(out, M, N, out_dtype, aq.device)
+    check(lib().mx_gemm_mxfp8(_ptr(aq), _ptr(as_), int(afmt), _ptr(bq), _ptr(bs), int(bfmt), M, N,
+                              K, int(alpha_exp), code, _ptr(out), out.stride(0), _stream(stream)),
+          "mx_gemm_mxfp8")
+    return out

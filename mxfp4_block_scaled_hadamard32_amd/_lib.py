@@ -16,6 +16,7 @@ MX_OK, MX_ERR_NULL, MX_ERR_SHAPE, MX_ERR_UNSUPPORTED, MX_ERR_LAUNCH, MX_ERR_ARG 
 MX_F32, MX_BF16 = 0, 1
 MX_SCALE_FLOOR, MX_SCALE_CEIL = 0, 1
 MX_ROUND_RNE, MX_ROUND_SR = 0, 1
+MX_E4M3, MX_E5M2 = 0, 1
 
 EXPORTS = ["mx_quantize", "mx_quantize_2d", "mx_dequantize", "mx_gemm_fprop", "mx_gemm_dgrad",
            "mx_gemm_wgrad", "mx_status_string", "mx_version"]
@@ -55,8 +56,12 @@ def lib() -> ctypes.CDLL:
         getattr(L, name).argtypes = gemm_args
     L.mx_gemm_fprop_quant.argtypes = [vp, vp, i32, vp, vp, i32, i64, i64, i64, i32,
                                       ctypes.POINTER(mx_quant_opts), vp, vp, vp]
+    L.mx_quantize_mxfp8.argtypes = [vp, i32, i64, i64, i64, i32, i32, ctypes.POINTER(mx_quant_opts),
+                                    vp, vp, vp]
+    L.mx_gemm_mxfp8.argtypes = [vp, vp, i32, vp, vp, i32, i64, i64, i64, i32, i32, vp, i64, vp]
     for name in ("mx_quantize", "mx_quantize_2d", "mx_dequantize", "mx_gemm_fprop",
-                 "mx_gemm_dgrad", "mx_gemm_wgrad", "mx_gemm_fprop_quant"):
+                 "mx_gemm_dgrad", "mx_gemm_wgrad", "mx_gemm_fprop_quant", "mx_quantize_mxfp8",
+                 "mx_gemm_mxfp8"):
         getattr(L, name).restype = ctypes.c_int
     L.mx_status_string.argtypes = [i32]
     L.mx_status_string.restype = ctypes.c_char_p

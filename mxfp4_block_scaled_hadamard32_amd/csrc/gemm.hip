@@ -8,11 +8,15 @@
 // blocks"; "Pretraining large language models with MXFP4", abstract: FP4 in Fprop, Dgrad and
 // Wgrad; "Training LLMs with MXFP4", abstract: MXFP4 GEMMs).
 //
-// Matrix-core facts used (gfx950 V_MFMA_SCALE_F32_32X32X64_F8F6F4 with FP4 operands):
-//  * operand lane l holds row (l % 32) and k = 32 * (l / 32) .. +31 of a 32x64 slice, as 16
-//    bytes, element 2i in the low nibble of byte i;
-//  * the 32-bit scale operand of lane l carries the E8M0 byte of exactly that 32-element
-//    k-block; the op_sel immediate picks which byte of the register is used;
+// Matrix-core facts used (gfx950 V_MFMA_SCALE_F32_32X32X64_F8F6F4; pinned on hardware by
+// single-instruction probes with random operands and scales):
+//  * FP4 operands: lane l holds row (l % 32) and k = 32 * (l / 32) .. +31 of a 32x64 slice,
+//    as 16 bytes, element 2i in the low nibble of byte i;
+//  * FP8 operands: lane l holds 32 bytes of row (l % 32): bytes 0-15 are 16 values of k-block
+//    0 and bytes 16-31 16 values of k-block 1 (which half of each block a lane holds only has
+//    to agree between the two operands; here lane half h holds k 16h .. 16h+15 of each);
+//  * the 32-bit scale operand of lane l carries the E8M0 byte of k-block (l / 32) of row
+//    l % 32; the op_sel immediate picks which byte of the register is used;
 //  * output register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l % 32.
 // Because every lane's 32 k-values form one scale block, the block scales enter the product
 // directly and the fp32 accumulation sees exact products.
@@ -85,6 +89,9 @@ __device__ __forceinline__ void static_for(F&& f) {
 __device__ __forceinline__ v8i as_operand(const u32x4& v) {
   return v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
 }
+
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ v8i as_operand(const u32x8& v) { return __builtin_bit_cast(v8i, v); }
 
 // Generic kernel (any K that is a multiple of 32): register-staged global loads. With
 // KFULL (K a multiple of 128) every step is complete and each row's 4 scale bytes of a step
@@ -327,11 +334,13 @@ __device__ __forceinline__ void wait_vmcnt() {
 // 64-byte row pieces; the L2 request rate, not its bandwidth, is what bounds this kernel.
 // WAVES = 4: one wave per SIMD, each wave owns 128x128 (4x4 MFMA tiles, 256 accumulators).
 // WAVES = 8: two waves per SIMD, each wave owns 64x128 (2x4 MFMA tiles).
-template <int WAVES, int BKS, int STAGES>
+template <int WAVES, int BKS, int STAGES, bool F8 = false>
 struct StreamCfg {
   static constexpr int kRow = 32 * BKS;                         // code bytes per row per stage
   static constexpr int kTile = kBM * kRow;                      // per operand
-  static constexpr int kScaleRow = 2 * BKS;                     // scale bytes per row per stage
+  static constexpr int kKStage = F8 ? kRow : 2 * kRow;          // k elements per stage
+  static constexpr int kSub = kKStage / 64;                     // 64-wide MFMA k sub-steps
+  static constexpr int kScaleRow = kKStage / 32;                // scale bytes per row per stage
   // BKS == 4: scales do not travel with the stage. A separate double-buffered area holds 4
   // steps (32 bytes) of scales per row, fetched as 32-byte pieces (one L2 request per row per
   // 4 steps instead of one per step); each step brings in one quarter of the next group.
@@ -343,9 +352,10 @@ struct StreamCfg {
   static constexpr int kLds = STAGES * kStage + (kGroupScales ? 2 * kGroupBytes : 0);
   static constexpr int kRowsPerBlock = 1024 / kRow;             // rows per 1 KiB code load
   static constexpr int kCodeLoads = kBM / kRowsPerBlock / WAVES;  // per operand per wave
-  // a group quarter (128 rows x 32 bytes) is split evenly over the waves: one 16-byte load
-  // per lane with 4 waves, two 4-byte loads per lane with 8 (there is no 8-byte direct load)
-  static constexpr int kGroupLaneBytes = WAVES == 4 ? 16 : 4;
+  // a group quarter (128 rows x kGroupRow bytes) is split evenly over the waves: one 16-byte
+  // load per lane for 32-byte FP4 rows with 4 waves, otherwise 4-byte loads (there is no
+  // 8-byte direct load)
+  static constexpr int kGroupLaneBytes = (WAVES == 4 && !F8) ? 16 : 4;
   static constexpr int kGroupLoads = kGroupBytes / 4 / WAVES / (64 * kGroupLaneBytes);
   static constexpr int kScaleLoads = kGroupScales ? kGroupLoads
                                                   : 2 * (kBM * kScaleRow / 256) / WAVES;
@@ -358,21 +368,31 @@ struct StreamCfg {
   }
 };
 
+// AF, BF: matrix-core element formats of A and B (4 = E2M1, packed two per byte; 0 = E4M3,
+// 1 = E5M2, one per byte). Both operands have the same width. With 8-bit elements a stage
+// holds half the k of the FP4 stage in the same bytes, and one MFMA (64 k) reads 32 bytes per
+// lane instead of 16 but takes twice as many cycles, so the bytes per MFMA cycle, the load
+// schedule and the LDS layout stay those of the FP4 kernel.
 template <int WAVES, int BKS, int STAGES, int SPLIT3 = 0, int SPLIT0 = 0, int SPLIT1 = 0,
-          bool QOUT = false>
+          bool QOUT = false, int AF = 4, int BF = 4>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(WAVES / 4, WAVES / 4)))
 void gemm_mx_stream_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, int lga,
                            const uint8_t* __restrict__ B, const uint8_t* __restrict__ Bs, int lgb,
                            int64_t M, int64_t N, int64_t K, float alpha_f, int out_bf16,
                            void* __restrict__ C, int64_t ldc, int nbm, int nbn,
                            GemmQuantOut qo) {
-  using Cfg = StreamCfg<WAVES, BKS, STAGES>;
+  constexpr bool F8 = AF != 4;
+  static_assert(F8 == (BF != 4), "both operands 4-bit or both 8-bit");
+  using Cfg = StreamCfg<WAVES, BKS, STAGES, F8>;
   static_assert(WAVES == 4 || WAVES == 8, "4 or 8 waves");
   static_assert((BKS == 2 && STAGES == 4) || (BKS == 4 && STAGES == 2), "stage shapes");
+  static_assert(!F8 || (BKS == 4 && !QOUT), "8-bit operands: 128-byte stages, plain output");
   constexpr int FA = WAVES == 4 ? 4 : 2;   // 32-row A fragments per wave
   constexpr int FB = 4;                    // 32-row B fragments per wave
   constexpr int WM = kBM / (32 * FA);      // waves along M
-  constexpr int SW = BKS / 2;              // scale words per row per stage
+  constexpr int SW = Cfg::kScaleRow / 4;   // scale words per row per stage
+  constexpr int NSUB = Cfg::kSub;          // MFMA k sub-steps per stage
+  using Frag = std::conditional_t<F8, u32x8, u32x4>;
   constexpr int LOADS = Cfg::kLoads;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg::kLds];
   uint8_t* const sgroup = smem + STAGES * Cfg::kStage;  // scale groups (BKS == 4)
@@ -393,8 +413,8 @@ void gemm_mx_stream_kernel(const uint8_t* __restrict__ A, const uint8_t* __restr
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int wm = wave % WM, wn = wave / WM;
-  const int64_t kbytes = K / 2, nkb = K / 32;
-  const int nk = (int)(K / (64 * BKS));
+  const int64_t kbytes = F8 ? K : K / 2, nkb = K / 32;
+  const int nk = (int)(K / Cfg::kKStage);
   const int frow = lane & 31, fhalf = lane >> 5;
 
   const int64_t rows_a = min((int64_t)kBM, M - m0), rows_b = min((int64_t)kBN, N - n0);
@@ -493,14 +513,24 @@ void gemm_mx_stream_kernel(const uint8_t* __restrict__ A, const uint8_t* __restr
       dma_b32(rs, dst, soff[j], ks * Cfg::kScaleRow);
     }
   };
-  auto lread = [&](const uint8_t* st, int sub, u32x4 (&fa)[FA], u32x4 (&fb)[FB]) {
+  // a lane's fragment of sub-step sub (64 k values of one row): FP4, the 32 values of k-block
+  // fhalf (16 bytes, chunk 2 sub + fhalf); FP8, 16 values of each k-block, the half fhalf of
+  // block 0 in bytes 0-15 and of block 1 in bytes 16-31 (chunks 4 sub + fhalf and
+  // 4 sub + 2 + fhalf)
+  auto frag = [&](const uint8_t* tile, int row, int sub) -> Frag {
+    if constexpr (F8) {
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(tile + Cfg::swz(row, 4 * sub + fhalf));
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(tile + Cfg::swz(row, 4 * sub + 2 + fhalf));
+      return u32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    } else {
+      return *reinterpret_cast<const u32x4*>(tile + Cfg::swz(row, 2 * sub + fhalf));
+    }
+  };
+  auto lread = [&](const uint8_t* st, int sub, Frag (&fa)[FA], Frag (&fb)[FB]) {
 #pragma unroll
-    for (int i = 0; i < FA; ++i)
-      fa[i] = *reinterpret_cast<const u32x4*>(st + Cfg::swz(wm * 32 * FA + 32 * i + frow, 2 * sub + fhalf));
+    for (int i = 0; i < FA; ++i) fa[i] = frag(st, wm * 32 * FA + 32 * i + frow, sub);
 #pragma unroll
-    for (int j = 0; j < FB; ++j)
-      fb[j] = *reinterpret_cast<const u32x4*>(st + Cfg::kTile +
-                                              Cfg::swz(wn * 32 * FB + 32 * j + frow, 2 * sub + fhalf));
+    for (int j = 0; j < FB; ++j) fb[j] = frag(st + Cfg::kTile, wn * 32 * FB + 32 * j + frow, sub);
   };
   // per-lane scale words of a stage: word w holds k-blocks 4w..4w+3 of the row; lanes 0-31
   // use the even blocks, lanes 32-63 the odd ones, so shift by one byte on the upper half and
@@ -538,7 +568,7 @@ void gemm_mx_stream_kernel(const uint8_t* __restrict__ A, const uint8_t* __restr
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
   // MFMAs of sub-step SUB: scale word SUB / 2, byte pair selected by op_sel 2 * (SUB % 2)
-  auto mma = [&](const u32x4 (&fa)[FA], const u32x4 (&fb)[FB], const uint32_t (&sa)[FA][SW],
+  auto mma = [&](const Frag (&fa)[FA], const Frag (&fb)[FB], const uint32_t (&sa)[FA][SW],
                  const uint32_t (&sb)[FB][SW], auto sub) {
     constexpr int SUB = decltype(sub)::value;
     constexpr int OP = 2 * (SUB % 2), W = SUB / 2;
@@ -547,10 +577,10 @@ void gemm_mx_stream_kernel(const uint8_t* __restrict__ A, const uint8_t* __restr
 #pragma unroll
       for (int j = 0; j < FB; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            as_operand(fb[j]), as_operand(fa[i]), acc[i][j], 4, 4, OP, sb[j][W], OP, sa[i][W]);
+            as_operand(fb[j]), as_operand(fa[i]), acc[i][j], BF, AF, OP, sb[j][W], OP, sa[i][W]);
   };
 
-  u32x4 fa0[FA], fb0[FB], fa1[FA], fb1[FB];
+  Frag fa0[FA], fb0[FB], fa1[FA], fb1[FB];
   uint32_t saC[FA][SW], sbC[FB][SW], saN[FA][SW], sbN[FB][SW];
 
   // Every step issues exactly LOADS loads per wave (steps past the end re-read step nk-1 into
@@ -573,9 +603,13 @@ void gemm_mx_stream_kernel(const uint8_t* __restrict__ A, const uint8_t* __restr
   // barrier, so that a full address queue stalls a single load rather than the whole sub-step.
   // Loads 0 .. kP3-1 go out during the last sub-step of step j-2 (right after its barrier),
   // the rest during sub-steps 0 .. 2 of step j-1; all of them land by the barrier of step j-1.
+  // FP4: at most one load per pair of MFMAs; FP8 (MFMAs twice as long): one per MFMA
+  constexpr int kPer = F8 ? 1 : 2;
   constexpr int kP3 = SPLIT3, kP0 = SPLIT0, kP1 = SPLIT1, kP2 = LOADS - kP3 - kP0 - kP1;
-  static_assert(STAGES != 2 || (kP2 >= 0 && 2 * kP3 <= FA * FB && 2 * kP0 <= FA * FB && 2 * kP1 <= FA * FB &&
-                2 * kP2 <= FA * FB), "at most one load per MFMA pair");
+  static_assert(STAGES != 2 || (kP2 >= 0 && kPer * kP3 <= FA * FB && kPer * kP0 <= FA * FB &&
+                kPer * kP1 <= FA * FB && kPer * kP2 <= FA * FB), "loads per sub-step");
+  static_assert(STAGES != 2 || NSUB == 4 || (NSUB == 2 && kP1 == 0 && kP2 == 0),
+                "two sub-steps: all loads in sub-steps 1 and 0");
   auto issue_load = [&](uint8_t* st, int j, int L) {
     if (L < Cfg::kScaleLoads) {
       issue_group_load((j + 3) / 4, (j + 3) % 4, L);
@@ -587,7 +621,7 @@ void gemm_mx_stream_kernel(const uint8_t* __restrict__ A, const uint8_t* __restr
   };
   // the same MFMAs with loads FIRST .. FIRST+CNT-1 of bundle j (into stage st) issued after
   // every second MFMA
-  auto mma_mix = [&](const u32x4 (&fa)[FA], const u32x4 (&fb)[FB], const uint32_t (&sa)[FA][SW],
+  auto mma_mix = [&](const Frag (&fa)[FA], const Frag (&fb)[FB], const uint32_t (&sa)[FA][SW],
                      const uint32_t (&sb)[FB][SW], auto sub, uint8_t* st, int j, auto first,
                      auto count) {
     constexpr int SUB = decltype(sub)::value;
@@ -596,9 +630,9 @@ void gemm_mx_stream_kernel(const uint8_t* __restrict__ A, const uint8_t* __restr
     static_for<FA * FB>([&](auto nn) {
       constexpr int n = decltype(nn)::value, i = n / FB, jj = n % FB;
       acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-          as_operand(fb[jj]), as_operand(fa[i]), acc[i][jj], 4, 4, OP, sb[jj][W], OP, sa[i][W]);
-      if constexpr (n % 2 == 1 && n / 2 < CNT) {
-        issue_load(st, j, FIRST + n / 2);
+          as_operand(fb[jj]), as_operand(fa[i]), acc[i][jj], BF, AF, OP, sb[jj][W], OP, sa[i][W]);
+      if constexpr (n % kPer == kPer - 1 && n / kPer < CNT) {
+        issue_load(st, j, FIRST + n / kPer);
         __builtin_amdgcn_sched_barrier(0);
       }
     });
@@ -628,9 +662,9 @@ void gemm_mx_stream_kernel(const uint8_t* __restrict__ A, const uint8_t* __restr
   // flight); every wave then holds all of stage ks in registers, so the stage is refilled at
   // once with step ks+STAGES; the scales and first sub-step of ks+1 are read meanwhile.
   auto body = [&](int ks, uint8_t* cur, const uint8_t* nxt) {
-    static_for<BKS>([&](auto sub) {
+    static_for<NSUB>([&](auto sub) {
       constexpr int S = decltype(sub)::value;
-      if constexpr (S + 1 < BKS) {
+      if constexpr (S + 1 < NSUB) {
         if constexpr (S % 2 == 0) lread(cur, S + 1, fa1, fb1);
         else lread(cur, S + 1, fa0, fb0);
       } else {
@@ -659,9 +693,9 @@ void gemm_mx_stream_kernel(const uint8_t* __restrict__ A, const uint8_t* __restr
   // Two-stage step ks on stage cur with the spread schedule: sub-steps 0 .. 2 carry the rest of
   // bundle ks+1 (into nxt), the last sub-step starts bundle ks+2 (into cur) after the barrier.
   auto body2 = [&](int ks, uint8_t* cur, uint8_t* nxt) {
-    static_for<BKS>([&](auto sub) {
+    static_for<NSUB>([&](auto sub) {
       constexpr int S = decltype(sub)::value;
-      if constexpr (S + 1 < BKS) {
+      if constexpr (S + 1 < NSUB) {
         constexpr int first = S == 0 ? kP3 : S == 1 ? kP3 + kP0 : kP3 + kP0 + kP1;
         constexpr int cnt = S == 0 ? kP0 : S == 1 ? kP1 : kP2;
         if constexpr (S % 2 == 0) {
@@ -674,7 +708,7 @@ void gemm_mx_stream_kernel(const uint8_t* __restrict__ A, const uint8_t* __restr
                   std::integral_constant<int, cnt>{});
         }
       } else {
-        static_assert(BKS % 2 == 0, "last sub-step uses fa1/fb1");
+        static_assert(NSUB % 2 == 0, "last sub-step uses fa1/fb1");
         __builtin_amdgcn_sched_barrier(0);
         wait_vmcnt<0>();
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage ks are done
@@ -910,4 +944,31 @@ hipError_t mx_launch_gemm_quant(const GemmArgs& g, const GemmQuantOut& q) {
                        dim3(64 * kStreamWaves), 0, (hipStream_t)g.stream, g.a, g.as, lga, g.b,
                        g.bs, lgb, g.M, g.N, g.K, alpha_f, 0, nullptr, 0, (int)nbm, (int)nbn, q);
   return hipGetLastError();
+}
+
+// MXFP8 operands (K a multiple of 128): the streaming kernel with 128-k stages; all but two
+// loads of a bundle go out during the last sub-step of the step before (one per MFMA)
+template <int AF, int BF>
+static hipError_t launch_gemm_fp8(const GemmArgs& g, const dim3 grid, float alpha_f, int lga,
+                                  int lgb, int nbm, int nbn) {
+  hipLaunchKernelGGL((gemm_mx_stream_kernel<4, 4, 2, 16, 2, 0, false, AF, BF>), grid, dim3(256), 0,
+                     (hipStream_t)g.stream, g.a, g.as, lga, g.b, g.bs, lgb, g.M, g.N, g.K, alpha_f,
+                     g.out_bf16 ? 1 : 0, g.c, g.ldc, nbm, nbn, GemmQuantOut{});
+  return hipGetLastError();
+}
+
+hipError_t mx_launch_gemm_fp8(const GemmArgs& g, int afmt, int bfmt) {
+  const int64_t nbm = (g.M + kBM - 1) / kBM, nbn = (g.N + kBN - 1) / kBN;
+  if (nbm * nbn > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if ((int64_t)kBM * g.K >= (int64_t)1 << 31) return hipErrorInvalidValue;
+  if (g.K <= 0 || g.K % 128 != 0) return hipErrorInvalidValue;
+  const float alpha_f = __builtin_bit_cast(float, (uint32_t)(g.alpha + 127) << 23);
+  const dim3 grid((unsigned)(nbm * nbn));
+  const int b = (afmt ? 2 : 0) | (bfmt ? 1 : 0);
+  switch (b) {
+    case 0: return launch_gemm_fp8<0, 0>(g, grid, alpha_f, 0, 0, (int)nbm, (int)nbn);
+    case 1: return launch_gemm_fp8<0, 1>(g, grid, alpha_f, 0, 0, (int)nbm, (int)nbn);
+    case 2: return launch_gemm_fp8<1, 0>(g, grid, alpha_f, 0, 0, (int)nbm, (int)nbn);
+    default: return launch_gemm_fp8<1, 1>(g, grid, alpha_f, 0, 0, (int)nbm, (int)nbn);
+  }
 }

@@ -143,6 +143,46 @@ mx_status mx_gemm_wgrad(const uint8_t* dytq, const uint8_t* dyts, int32_t gdy, c
   return gemm(dytq, dyts, gdy, xtq, xts, gx, N, K, T, alpha_exp, out_dtype, dw, ldw, stream);
 }
 
+mx_status mx_quantize_mxfp8(const void* x, int32_t dtype, int64_t rows, int64_t cols, int64_t ld,
+                            int32_t axis, int32_t fmt, const mx_quant_opts* opts, uint8_t* codes,
+                            uint8_t* scales, void* stream) {
+  mx_status s = check_opts(opts);
+  if (s != MX_OK) return s;
+  if (axis != 0 && axis != 1) return MX_ERR_ARG;
+  if (fmt != MX_E4M3 && fmt != MX_E5M2) return MX_ERR_ARG;
+  if ((s = check_source(x, dtype, rows, cols, ld)) != MX_OK) return s;
+  if (axis == 1 && cols % 32 != 0) return MX_ERR_SHAPE;
+  if (axis == 0 && (rows % 32 != 0 || cols % 8 != 0)) return MX_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return MX_OK;
+  if (!x || !codes || !scales) return MX_ERR_NULL;
+  // rows: 8 code bytes per lane; columns: 16-byte pieces of transposed code rows
+  if (!aligned(codes, axis == 1 ? 8 : 16)) return MX_ERR_ARG;
+  QuantArgs a{x, dtype == MX_BF16, rows, cols, ld, axis, opts->scale_rule == MX_SCALE_CEIL,
+              opts->round == MX_ROUND_SR, opts->hadamard == 1, opts->sign_mask, opts->seed,
+              codes, scales, nullptr, nullptr, stream};
+  return launch_status(mx_launch_quantize_fp8(a, fmt));
+}
+
+mx_status mx_gemm_mxfp8(const uint8_t* aq, const uint8_t* as, int32_t afmt, const uint8_t* bq,
+                        const uint8_t* bs, int32_t bfmt, int64_t M, int64_t N, int64_t K,
+                        int32_t alpha_exp, int32_t out_dtype, void* c, int64_t ldc, void* stream) {
+  if (M < 0 || N < 0 || K < 0) return MX_ERR_SHAPE;
+  if (M % 32 || N % 32 || K % 32) return MX_ERR_SHAPE;
+  if (ldc < N || ldc % 8 != 0) return MX_ERR_SHAPE;
+  if ((afmt != MX_E4M3 && afmt != MX_E5M2) || (bfmt != MX_E4M3 && bfmt != MX_E5M2)) return MX_ERR_ARG;
+  if (out_dtype != MX_F32 && out_dtype != MX_BF16) return MX_ERR_ARG;
+  if (alpha_exp < -126 || alpha_exp > 127) return MX_ERR_ARG;
+  if (M == 0 || N == 0) return MX_OK;
+  if (!c) return MX_ERR_NULL;
+  if (!aligned(c, 16)) return MX_ERR_ARG;
+  GemmArgs g{aq, as, 1, bq, bs, 1, M, N, K, alpha_exp, out_dtype == MX_BF16, c, ldc, stream};
+  if (K == 0) return launch_status(mx_launch_gemm(g));  // an empty sum: the output is zero
+  if (K % 128 != 0) return MX_ERR_UNSUPPORTED;
+  if (!aq || !as || !bq || !bs) return MX_ERR_NULL;
+  if (!aligned(aq, 16) || !aligned(bq, 16)) return MX_ERR_ARG;
+  return launch_status(mx_launch_gemm_fp8(g, afmt, bfmt));
+}
+
 const char* mx_status_string(int32_t status) {
   switch (status) {
     case MX_OK: return "MX_OK";

@@ -248,4 +248,132 @@ __device__ __forceinline__ void transpose_nibbles8x8(uint32_t (&R)[8]) {
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// MXFP8 [P3 "The fix, and its supporting cast": queries and keys in MXFP8]: the E8M0 scale of
+// the FP4 path with 8-bit elements, E4M3 (FMT 0: bias 7, 3 mantissa bits, largest 448, no
+// infinity) or E5M2 (FMT 1: bias 15, 2 mantissa bits, largest 57344), the OCP MX encodings.
+// ---------------------------------------------------------------------------------------------
+template <int FMT>
+struct Fp8 {
+  static constexpr int kMant = FMT == 0 ? 3 : 2;
+  static constexpr int kBias = FMT == 0 ? 7 : 15;
+  static constexpr int kEmax = FMT == 0 ? 8 : 15;            // exponent of the largest value
+  static constexpr uint32_t kLargest = FMT == 0 ? 0x43E00000u : 0x47600000u;  // 448, 57344
+  static constexpr uint32_t kTop = FMT == 0 ? 0x7Eu : 0x7Bu;  // its code
+  static constexpr int kMinNormal = 1 - kBias;                 // exponent of the least normal
+};
+
+// scale byte from the block maximum's bits: floor e = F - 127 - emax; ceil adds one when the
+// mantissa exceeds 1.75 (the largest value is 1.75 * 2^emax); clamped at 0; non-finite -> 0xFF
+template <bool CEIL, int FMT>
+__device__ __forceinline__ uint32_t scale_byte_fp8(uint32_t amax_bits) {
+  if (amax_bits >= 0x7F800000u) return 0xFFu;
+  int32_t b = (int32_t)(amax_bits >> 23) - Fp8<FMT>::kEmax;
+  if (CEIL) b += (amax_bits & 0x7FFFFFu) > 0x600000u ? 1 : 0;
+  return (uint32_t)(b < 0 ? 0 : b);
+}
+
+// Rounding to the element format, on gfx950's converters (unit scale). Values are first
+// clamped to +-largest (saturation; the converters themselves are not used beyond it).
+// Nearest-even: v_cvt_scalef32_pk_fp8_f32 / _bf8_f32, two values per instruction (the first in
+// the low byte). Stochastic: v_cvt_scalef32_sr_fp8_f32 / _bf8_f32 rounds the magnitude up iff
+// floor(f * 2^d) + (R >> (32 - d)) >= 2^d, where f is the position of |v| between its two
+// neighbours and d = 23 - mantissa bits; with R = (~r << 16) | 0xFFFF that is floor(f * 2^d) >
+// 2^(d - 16) r, the rule r < f * 2^16 once f * 2^d is an integer. In the normal range it is
+// (the d dropped significand bits). Below the least normal the step stays 2^(min - mant), so
+// |v| is first rounded up to a multiple of 2^(min - mant - d) (2^-29 for E4M3, 2^-37 grid
+// refined to 2^-36 for E5M2); the thresholds lo + r 2^(min - mant - 16) lie on that grid, so
+// the rounding up moves no value across one. Both were checked bit for bit against the
+// integer definition over every bf16 value at five scales, random fp32 values, and random and
+// extreme fields.
+typedef short v2s_fp8 __attribute__((ext_vector_type(2)));
+
+template <int FMT>
+__device__ __forceinline__ float fp8_clamp(float v) {
+  const float lim = __uint_as_float(Fp8<FMT>::kLargest);
+  return __builtin_amdgcn_fmed3f(v, -lim, lim);
+}
+
+template <int FMT>
+__device__ __forceinline__ uint32_t fp8_rne_pair(float a, float b) {
+  v2s_fp8 o = {0, 0};
+  if (FMT == 0) o = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, fp8_clamp<FMT>(a), fp8_clamp<FMT>(b), 1.0f, false);
+  else o = __builtin_amdgcn_cvt_scalef32_pk_bf8_f32(o, fp8_clamp<FMT>(a), fp8_clamp<FMT>(b), 1.0f, false);
+  return (uint32_t)(uint16_t)o.x;
+}
+
+template <int FMT>
+__device__ __forceinline__ uint32_t fp8_sr_byte(float v, uint32_t r) {
+  v = fp8_clamp<FMT>(v);
+  const float a = fabsf(v);
+  constexpr float kMinNormal = FMT == 0 ? 0x1p-6f : 0x1p-14f;
+  constexpr float kUp = FMT == 0 ? 0x1p29f : 0x1p36f;
+  constexpr float kDown = FMT == 0 ? 0x1p-29f : 0x1p-36f;
+  const float up = a < kMinNormal ? __builtin_ceilf(a * kUp) * kDown : a;
+  const float vv = __builtin_copysignf(up, v);
+  const uint32_t R = (~r << 16) | 0xFFFFu;
+  const uint32_t w = FMT == 0 ? __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(0u, vv, R, 1.0f, 0)
+                              : __builtin_amdgcn_cvt_scalef32_sr_bf8_f32(0u, vv, R, 1.0f, 0);
+  return w & 0xFFu;
+}
+
+// raw 16-bit random fields of source elements 8g .. 8g+7 (field k: the low half of Philox
+// output word k / 2 for even k, the high half for odd k)
+__device__ __forceinline__ void sr_fields8(uint64_t g, uint64_t seed, uint32_t (&r)[8]) {
+  const uint4 w = philox4x32_10((uint32_t)g, (uint32_t)(g >> 32), 0u, 0u, (uint32_t)seed,
+                                (uint32_t)(seed >> 32));
+  const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r[2 * i] = wd[i] & 0xFFFFu;
+    r[2 * i + 1] = wd[i] >> 16;
+  }
+}
+
+// 8 scaled values -> 8 code bytes (value k in byte k of the pair of words)
+template <int FMT, bool SR>
+__device__ __forceinline__ uint2 fp8_pack8(const float (&v)[8], const uint32_t (&r)[8]) {
+  uint32_t w[2] = {0u, 0u};
+  if (SR) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) w[k >> 2] |= fp8_sr_byte<FMT>(v[k], r[k]) << (8 * (k & 3));
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; k += 2) w[k >> 2] |= fp8_rne_pair<FMT>(v[k], v[k + 1]) << (8 * (k & 3));
+  }
+  return make_uint2(w[0], w[1]);
+}
+
+// The MXFP8 counterpart of quant_chunk8: one lane's 8 values of a 1x32 block held by a quad;
+// returns the 8 code bytes, sb gets the block's scale byte.
+template <int FMT, bool HAD, bool SR, bool CEIL>
+__device__ __forceinline__ uint2 quant_chunk8_fp8(float (&w)[8], int q, uint32_t sign_mask,
+                                                  uint64_t seed, uint64_t g, uint32_t& sb) {
+  if (HAD) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      w[k] = __uint_as_float(__float_as_uint(w[k]) ^ (((sign_mask >> (8 * q + k)) & 1u) << 31));
+    fwht8_inlane(w);
+    const uint32_t up8 = (q & 1) ? 0x80000000u : 0u;
+    const uint32_t up16 = (q & 2) ? 0x80000000u : 0u;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) w[k] = butterfly_xlane<kQuadXor1>(w[k], up8);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) w[k] = butterfly_xlane<kQuadXor2>(w[k], up16);
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) m = max(m, abs_bits(w[k]));
+  m = max(m, dpp_u32<kQuadXor1>(m));
+  m = max(m, dpp_u32<kQuadXor2>(m));
+  sb = scale_byte_fp8<CEIL, FMT>(m);
+  if (sb == 0xFFu) return make_uint2(0u, 0u);
+  const float inv = inv_scale_from_byte(sb);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) w[k] = w[k] * inv;
+  uint32_t r[8];
+  if (SR) sr_fields8(g, seed, r);
+  return fp8_pack8<FMT, SR>(w, r);
+}
+
 }  // namespace mxd

@@ -22,6 +22,9 @@ struct QuantArgs {
 
 hipError_t mx_launch_quantize(const QuantArgs& a);
 hipError_t mx_launch_quantize_2d(const QuantArgs& a);
+// MXFP8 1x32 quantize (fmt 0 = E4M3, 1 = E5M2): codes one byte per element,
+// axis 1: [rows][cols], axis 0: [cols][rows]; scales as for MXFP4
+hipError_t mx_launch_quantize_fp8(const QuantArgs& a, int fmt);
 hipError_t mx_launch_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows,
                                 int64_t cols, int block_rows, int inv_had, uint32_t sign_mask,
                                 float* out, void* stream);
@@ -57,3 +60,7 @@ struct GemmQuantOut {
 
 // K must be a multiple of 128 (the streaming kernels); returns hipErrorInvalidValue otherwise.
 hipError_t mx_launch_gemm_quant(const GemmArgs& g, const GemmQuantOut& q);
+
+// MXFP8 GEMM: A [M][K], B [N][K] one code byte per element (afmt / bfmt: 0 = E4M3, 1 = E5M2),
+// scales [M][K/32] and [N][K/32] (ga = gb = 1). K must be a positive multiple of 128.
+hipError_t mx_launch_gemm_fp8(const GemmArgs& g, int afmt, int bfmt);

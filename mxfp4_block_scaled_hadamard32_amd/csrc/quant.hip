@@ -348,6 +348,130 @@ __global__ __launch_bounds__(kThreads) void quant_2d_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------
+// MXFP8 [P3 "The fix, and its supporting cast": queries and keys in MXFP8]: the same block
+// structure with one code byte per element (E4M3 or E5M2). Along rows a lane's 8 codes are 8
+// consecutive output bytes; down the columns a lane's 8 codes of one column go to an LDS tile
+// of 256 bytes per column (the tile's 256 rows), which leaves as whole 256-byte pieces.
+// ---------------------------------------------------------------------------------------------
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <int FMT, bool BF16, bool HAD, bool SR, bool CEIL>
+__global__ __launch_bounds__(kThreads) void quant_rows_fp8_kernel(
+    const void* __restrict__ x, int64_t nchunks, int64_t cpr, int64_t ld, int contiguous,
+    uint32_t sign_mask, uint64_t seed, u32x2* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const int q = threadIdx.x & 3;
+  const int64_t base = (int64_t)blockIdx.x * (kThreads * kRowChunksPerThread) + threadIdx.x;
+  float v[kRowChunksPerThread][8];
+#pragma unroll
+  for (int u = 0; u < kRowChunksPerThread; ++u) {
+    const int64_t g = base + (int64_t)u * kThreads;
+    if (g < nchunks) {
+      int64_t off = 8 * g;
+      if (!contiguous) {
+        const int64_t r = g / cpr;
+        off = r * ld + 8 * (g - r * cpr);
+      }
+      load8<BF16>(x, off, v[u]);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kRowChunksPerThread; ++u) {
+    const int64_t g = base + (int64_t)u * kThreads;
+    if (g >= nchunks) continue;  // quads are all in or all out (cols % 32 == 0)
+    uint32_t sb;
+    const uint2 w = quant_chunk8_fp8<FMT, HAD, SR, CEIL>(v[u], q, sign_mask, seed, (uint64_t)g, sb);
+    __builtin_nontemporal_store(u32x2{w.x, w.y}, codes + g);
+    if (q == 0) scales[g >> 2] = (uint8_t)sb;
+  }
+}
+
+constexpr int kCodeStride8 = 272;  // LDS bytes per column of the FP8 code tile (256 + 16)
+
+template <int FMT, bool BF16, bool HAD, bool SR, bool CEIL>
+__global__ __launch_bounds__(kThreads) void quant_cols_fp8_kernel(
+    const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, uint32_t sign_mask,
+    uint64_t seed, uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t, int64_t n_rt,
+    int64_t n_ct) {
+  __shared__ __attribute__((aligned(16))) uint8_t ctile[kColTileCols * kCodeStride8];
+  __shared__ __attribute__((aligned(16))) uint8_t stile[kColTileCols * 8];
+  int64_t rt, ct;
+  if (!col_tile_of(n_rt, n_ct, rt, ct)) return;  // uniform per workgroup
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int q = lane & 3, cg = lane >> 2;
+  const int64_t rb0 = rt * 8;
+  const int nrb = (int)min((int64_t)8, rows / 32 - rb0);
+  const int64_t ctile0 = ct * kColTileCols;
+
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int rbl = pass * 4 + wave;
+    const int64_t c0 = ctile0 + cg * 8;
+    if (rbl >= nrb || c0 >= cols) continue;  // whole quads leave together
+    const int64_t r0 = (rb0 + rbl) * 32 + 8 * q;
+    float p[8][8];
+    load_patch<BF16>(x, ld, r0, c0, p);
+    if (HAD) fwht_columns(p, sign_mask, q);
+
+    uint32_t sb[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      uint32_t m = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m = max(m, abs_bits(p[j][k]));
+      m = max(m, dpp_u32<kQuadXor1>(m));
+      m = max(m, dpp_u32<kQuadXor2>(m));
+      sb[k] = scale_byte_fp8<CEIL, FMT>(m);
+    }
+    uint32_t r[8][8];  // r[j][k]: random field of patch element (j, k)
+    if (SR) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sr_fields8((uint64_t)((r0 + j) * cols + c0) >> 3, seed, r[j]);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      uint2 w = make_uint2(0u, 0u);
+      if (sb[k] != 0xFFu) {
+        const float inv = inv_scale_from_byte(sb[k]);
+        float col[8];
+        uint32_t rc[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          col[j] = p[j][k] * inv;
+          rc[j] = SR ? r[j][k] : 0u;
+        }
+        w = fp8_pack8<FMT, SR>(col, rc);
+      }
+      const int cl = cg * 8 + k;  // column within the tile
+      *reinterpret_cast<u32x2*>(ctile + cl * kCodeStride8 + rbl * 32 + 8 * q) = u32x2{w.x, w.y};
+      if (q == 0) stile[cl * 8 + rbl] = (uint8_t)sb[k];
+    }
+  }
+  __syncthreads();
+
+  // codes: 16 lanes per column, 16 bytes each, so one store instruction writes the 256-byte
+  // pieces of 4 columns
+#pragma unroll
+  for (int round = 0; round < kColTileCols * 16 / kThreads; ++round) {
+    const int c = round * (kThreads / 16) + (threadIdx.x >> 4), piece = threadIdx.x & 15;
+    if (ctile0 + c < cols && piece < 2 * nrb)
+      __builtin_nontemporal_store(
+          *reinterpret_cast<const u32x4*>(ctile + c * kCodeStride8 + 16 * piece),
+          reinterpret_cast<u32x4*>(codes_t + (ctile0 + c) * rows + rb0 * 32 + 16 * piece));
+  }
+  for (int cs = threadIdx.x; cs < kColTileCols; cs += kThreads) {
+    if (ctile0 + cs >= cols) break;
+    uint8_t* dst = scales_t + (ctile0 + cs) * (rows / 32) + rb0;
+    const uint8_t* src = stile + cs * 8;
+    if (nrb == 8 && ((reinterpret_cast<uintptr_t>(dst) & 7) == 0)) {
+      *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(src);
+    } else {
+      for (int i = 0; i < nrb; ++i) dst[i] = src[i];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // Dequantize: out = E2M1(code) * 2^(byte-127) in fp32; optional inverse rotation (1/32) D H
 // per 32-block along the row. One lane per 8 elements, flat over the tensor.
 // ---------------------------------------------------------------------------------------------
@@ -459,6 +583,43 @@ hipError_t pick_2d(const QuantArgs& a) {
   return a.ceil ? launch_2d<BF16, false, true>(a) : launch_2d<BF16, false, false>(a);
 }
 
+template <int FMT, bool BF16, bool HAD, bool SR, bool CEIL>
+hipError_t launch_fp8(const QuantArgs& a) {
+  if (a.axis == 1) {
+    const int64_t cpr = a.cols / 8;
+    const int64_t nchunks = a.rows * cpr;
+    const int64_t per_block = kThreads * kRowChunksPerThread;
+    const int64_t nblocks = (nchunks + per_block - 1) / per_block;
+    if (nblocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((quant_rows_fp8_kernel<FMT, BF16, HAD, SR, CEIL>), dim3((unsigned)nblocks),
+                       dim3(kThreads), 0, (hipStream_t)a.stream, a.x, nchunks, cpr, a.ld,
+                       a.ld == a.cols ? 1 : 0, a.sign_mask, a.seed,
+                       reinterpret_cast<u32x2*>(a.codes), a.scales);
+  } else {
+    int64_t n_rt, n_ct;
+    const int64_t nblocks = col_tile_grid(a.rows, a.cols, n_rt, n_ct);
+    if (nblocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((quant_cols_fp8_kernel<FMT, BF16, HAD, SR, CEIL>), dim3((unsigned)nblocks),
+                       dim3(kThreads), 0, (hipStream_t)a.stream, a.x, a.rows, a.cols, a.ld,
+                       a.sign_mask, a.seed, a.codes, a.scales, n_rt, n_ct);
+  }
+  return hipGetLastError();
+}
+
+template <int FMT, bool BF16, bool HAD>
+hipError_t pick_fp8_rule(const QuantArgs& a) {
+  if (a.sr) return a.ceil ? launch_fp8<FMT, BF16, HAD, true, true>(a)
+                          : launch_fp8<FMT, BF16, HAD, true, false>(a);
+  return a.ceil ? launch_fp8<FMT, BF16, HAD, false, true>(a)
+                : launch_fp8<FMT, BF16, HAD, false, false>(a);
+}
+
+template <int FMT>
+hipError_t pick_fp8(const QuantArgs& a) {
+  if (a.bf16) return a.hadamard ? pick_fp8_rule<FMT, true, true>(a) : pick_fp8_rule<FMT, true, false>(a);
+  return a.hadamard ? pick_fp8_rule<FMT, false, true>(a) : pick_fp8_rule<FMT, false, false>(a);
+}
+
 }  // namespace
 
 hipError_t mx_launch_quantize(const QuantArgs& a) {
@@ -478,4 +639,8 @@ hipError_t mx_launch_dequantize(const uint8_t* codes, const uint8_t* scales, int
                      reinterpret_cast<const uint32_t*>(codes), scales, rows, cols, block_rows,
                      inv_had, sign_mask, out);
   return hipGetLastError();
+}
+
+hipError_t mx_launch_quantize_fp8(const QuantArgs& a, int fmt) {
+  return fmt == 0 ? pick_fp8<0>(a) : pick_fp8<1>(a);
 }

@@ -24,16 +24,18 @@ def bf16_round_f64(x: np.ndarray) -> np.ndarray:
     return out
 
 
-def check_gemm(gpu: torch.Tensor, C: np.ndarray, Cabs: np.ndarray, rows=None, cols=None):
-    """fp32 output: elementwise |gpu - C| <= 2^-20 Cabs. bf16 output: the rounding of any value
-    within that bound, i.e. RNE(C - b) <= gpu <= RNE(C + b) (rounding is monotone)."""
+def check_gemm(gpu: torch.Tensor, C: np.ndarray, Cabs: np.ndarray, rows=None, cols=None,
+               rel: float = GEMM_REL):
+    """fp32 output: elementwise |gpu - C| <= rel * Cabs (rel = 2^-20 by default). bf16 output:
+    the rounding of any value within that bound, i.e. RNE(C - b) <= gpu <= RNE(C + b) (rounding
+    is monotone)."""
     g = gpu
     if rows is not None:
         g = g[torch.as_tensor(rows, device=g.device)]
     if cols is not None:
         g = g[:, torch.as_tensor(cols, device=g.device)]
     got = g.float().cpu().numpy().astype(np.float64)
-    bound = GEMM_REL * Cabs
+    bound = rel * Cabs
     if gpu.dtype == torch.float32:
         err = np.abs(got - C)
         bad = ~(err <= bound)

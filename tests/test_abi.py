@@ -128,3 +128,41 @@ def test_gemm_fprop_quant_argument_errors(L):
     assert call(xq=None) == m.MX_ERR_NULL
     assert call(yq=ctypes.c_void_p(0x10002)) == m.MX_ERR_ARG
     assert call(T=0, yq=None, ys=None) == m.MX_OK
+
+
+def test_quantize_mxfp8_argument_errors(L):
+    from mxfp4_block_scaled_hadamard32_amd import _lib as m
+    q = L.mx_quantize_mxfp8
+
+    def call(x=FAKE, dt=1, rows=64, cols=64, ld=64, axis=1, fmt=0, o=None, codes=FAKE, scales=FAKE):
+        return q(x, dt, rows, cols, ld, axis, fmt, opts() if o is None else o, codes, scales, None)
+    assert call(cols=48, ld=48) == m.MX_ERR_SHAPE             # cols % 32 along rows
+    assert call(rows=48, axis=0) == m.MX_ERR_SHAPE            # rows % 32 down columns
+    assert call(rows=64, cols=36, ld=40, axis=0) == m.MX_ERR_SHAPE  # cols % 8 down columns
+    assert call(fmt=2) == m.MX_ERR_ARG
+    assert call(axis=3) == m.MX_ERR_ARG
+    assert call(o=opts(hadamard=2)) == m.MX_ERR_ARG
+    assert q(FAKE, 1, 64, 64, 64, 1, 0, None, FAKE, FAKE, None) == m.MX_ERR_NULL
+    assert call(scales=None) == m.MX_ERR_NULL
+    assert call(codes=ctypes.c_void_p(0x10004)) == m.MX_ERR_ARG          # 8-byte rule (rows)
+    assert call(codes=ctypes.c_void_p(0x10008), axis=0) == m.MX_ERR_ARG  # 16-byte rule (cols)
+    assert call(x=None, rows=0, codes=None, scales=None) == m.MX_OK
+
+
+def test_gemm_mxfp8_argument_errors(L):
+    from mxfp4_block_scaled_hadamard32_amd import _lib as m
+    g = L.mx_gemm_mxfp8
+
+    def call(M=64, N=64, K=128, af=0, bf=1, alpha=0, dt=1, c=FAKE, ldc=64, a=FAKE):
+        return g(a, FAKE, af, FAKE, FAKE, bf, M, N, K, alpha, dt, c, ldc, None)
+    assert call(M=40) == m.MX_ERR_SHAPE
+    assert call(K=48) == m.MX_ERR_SHAPE
+    assert call(K=96) == m.MX_ERR_UNSUPPORTED   # 128-k stages
+    assert call(ldc=66) == m.MX_ERR_SHAPE
+    assert call(af=2) == m.MX_ERR_ARG and call(bf=-1) == m.MX_ERR_ARG
+    assert call(dt=5) == m.MX_ERR_ARG
+    assert call(alpha=128) == m.MX_ERR_ARG
+    assert call(c=None) == m.MX_ERR_NULL
+    assert call(a=None) == m.MX_ERR_NULL
+    assert call(c=ctypes.c_void_p(0x10008)) == m.MX_ERR_ARG
+    assert call(N=0, c=None) == m.MX_OK

@@ -121,3 +121,13 @@ def llama70b_down(device="cpu", T: int = 16384, D: int = 8192, F: int = 28672):
     W = normal((D, F), 0.01, seed=51, device=device)
     dY = normal((T, D), 1e-3, seed=52, device=device)
     return {"H": to_bf16(H), "W": to_bf16(W), "dY": to_bf16(dY)}
+
+
+def llama70b_attn_q(device="cpu", T: int = 16384, D: int = 8192, N: int = 8192):
+    """Attention query projection of the 70B model, one GPU's share: X [T][D] ~ t(3) (the
+    normalised layer input), Wq [N][D] ~ N(0, 0.01), dY [T][N] ~ N(0, 1e-3). N = 1024 gives the
+    key projection (8 key/value heads of 128)."""
+    X = student_t3((T, D), seed=60, device=device)
+    W = normal((N, D), 0.01, seed=61, device=device)
+    dY = normal((T, N), 1e-3, seed=62, device=device)
+    return {"X": to_bf16(X), "W": to_bf16(W), "dY": to_bf16(dY)}
