@@ -53,6 +53,8 @@ def parse():
     p.add_argument("--step-only", action="store_true",
                    help="skip the comparisons run after the timed steps (fused epilogue, linear "
                         "layer), so that a profile of the run holds the step's launches alone")
+    p.add_argument("--with-mxfp8", action="store_true",
+                   help="with --step-only, still run the MXFP8 attention-projection comparison")
     p.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="no GPU work: turn the counter_collection.csv files of a FETCH_SIZE and "
                         "a WRITE_SIZE rocprofv3 pass over a --copy-calibration run into the "
@@ -250,6 +252,58 @@ def linear_layer(layer, torch, reps: int = 3):
     return res
 
 
+PEAK_FP8_TFLOPS = 5000.0     # MI355X dense MXFP8 matrix-core peak
+FP8_QUANT_BYTES_PER_ELEM = 2 + 1 + 1 / 32  # bf16 in, one code byte, one scale byte per 32
+
+
+def mxfp8_attention(mx, wl, torch, reps: int = 5):
+    """Outside the timed step: the MXFP8 variant for the attention query projection of the 70B
+    model, one GPU's share (X 16384x8192, Wq 8192x8192, dY 16384x8192, bf16): X and Wq in E4M3,
+    dY in E5M2, ceil scale, nearest-even; the X-along-K quantization and the three GEMMs."""
+    d = wl.llama70b_attn_q(device="cuda")
+    X, W, dY = d["X"], d["W"], d["dY"]
+    T, D = X.shape
+    N = W.shape[0]
+    q = mx.mx_quantize_mxfp8
+    xq, xs = q(X, fmt=0, scale_rule=1)
+    wq, ws = q(W, fmt=0, scale_rule=1)
+    wtq, wts = q(W, fmt=0, axis=0, scale_rule=1)
+    dyq, dys = q(dY, fmt=1, scale_rule=1)
+    dytq, dyts = q(dY, fmt=1, axis=0, scale_rule=1)
+    xtq, xts = q(X, fmt=0, axis=0, scale_rule=1)
+    bf = torch.bfloat16
+    y = torch.empty((T, N), dtype=bf, device="cuda")
+    dx = torch.empty((T, D), dtype=bf, device="cuda")
+    dw = torch.empty((N, D), dtype=bf, device="cuda")
+    runs = [("quant_x_rows", lambda: q(X, fmt=0, scale_rule=1, codes=xq, scales=xs)),
+            ("fprop", lambda: mx.mx_gemm_mxfp8(xq, xs, 0, wq, ws, 0, out=y)),
+            ("dgrad", lambda: mx.mx_gemm_mxfp8(dyq, dys, 1, wtq, wts, 0, out=dx)),
+            ("wgrad", lambda: mx.mx_gemm_mxfp8(dytq, dyts, 1, xtq, xts, 0, out=dw))]
+    flops = 2.0 * T * D * N
+    res = {"mxfp8_workload": "70B attention query projection, T=16384, D=8192, N=8192; "
+                             "X, Wq E4M3, dY E5M2; ceil scale, RNE"}
+    for name, fn in runs:
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        res[f"mxfp8_{name}_ms"] = round(ms, 4)
+        if name == "quant_x_rows":
+            gbs = T * D * FP8_QUANT_BYTES_PER_ELEM / (ms * 1e-3) / 1e9
+            res["mxfp8_quant_x_rows_gbs"] = round(gbs, 1)
+            res["mxfp8_quant_x_rows_pct_of_hbm_peak"] = round(100.0 * gbs / PEAK_HBM_GBS, 2)
+        else:
+            tf = flops / (ms * 1e-3) / 1e12
+            res[f"mxfp8_{name}_tflops"] = round(tf, 1)
+            res[f"mxfp8_{name}_pct_of_fp8_peak"] = round(100.0 * tf / PEAK_FP8_TFLOPS, 2)
+    return res
+
+
 COPY_BYTES = 1 << 30  # the --copy-calibration copy reads and writes 1 GiB
 
 
@@ -291,9 +345,10 @@ def write_traffic(fetch_csv: str, write_csv: str, workload: str):
     wf = COPY_BYTES / (copy_value(write) * 1024.0)
 
     def gemm_value(table, wgs):
-        # the plain-output GEMM (last template argument false), not the quantizing epilogue
+        # the MXFP4 GEMM with plain output (template arguments ..., QOUT false, A and B
+        # formats 4), not the quantizing epilogue or the MXFP8 kernel
         vals = [vs for (name, g), vs in table.items()
-                if re.search(r"gemm_mx\w*<[^>]*false>", name) and g == wgs]
+                if re.search(r"gemm_mx\w*<[^>]*false, 4, 4>", name) and g == wgs]
         if len(vals) != 1:
             raise SystemExit(f"expected one GEMM kernel with {wgs} workgroups, found {len(vals)}")
         return sum(vals[0]) / len(vals[0])
@@ -301,10 +356,10 @@ def write_traffic(fetch_csv: str, write_csv: str, workload: str):
     rec = {"gemm_sha": sha(GEMM_SRC), "fetch_factor": ff, "write_factor": wf,
            "command_fetch": ("rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch "
                              "-o run -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline "
-                             "--step-only --copy-calibration"),
+                             "--step-only --with-mxfp8 --copy-calibration"),
            "command_write": ("rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write "
                              "-o run -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline "
-                             "--step-only --copy-calibration")}
+                             "--step-only --with-mxfp8 --copy-calibration")}
     for name, M, Nn, Kk in (("fprop", T, N, K), ("dgrad", T, K, N), ("wgrad", N, K, T)):
         wgs = ((M + 255) // 256) * ((Nn + 255) // 256)
         hbm = gemm_value(fetch, wgs) * 1024.0 * ff + gemm_value(write, wgs) * 1024.0 * wf
@@ -403,6 +458,8 @@ def main():
     if not args.step_only:
         out["components"].update(fused_epilogue(layer, torch))
         out["components"].update(linear_layer(layer, torch))
+    if not args.step_only or args.with_mxfp8:
+        out["components"].update(mxfp8_attention(mx, wl, torch))
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         cb = cpu_baseline(layer, args.cpu_sample_rows)
