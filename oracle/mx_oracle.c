@@ -297,6 +297,47 @@ int orc_quantize_2d(const void* x, int dtype, int64_t rows, int64_t cols, int64_
 }
 
 /* ------------------------------------------------------------------------------------------ */
+/* BxB tiles, B in {8, 32, 64} [P3 "The fix ...": Table 4 compares 8x8, 32x32 and 64x64       */
+/* blocks]: the 32x32 rule with another tile edge. One scale per tile from the tile maximum;   */
+/* codes[rows][cols/2], scales[rows/B][cols/B], and the transposed copies codes_t[cols][rows/2],*/
+/* scales_t[cols/B][rows/B] (nullable). Rows [row_begin, row_end), multiples of B.             */
+/* ------------------------------------------------------------------------------------------ */
+int orc_quantize_2d_block(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                          int B, const orc_opts* o, uint8_t* codes, uint8_t* scales,
+                          uint8_t* codes_t, uint8_t* scales_t, int64_t row_begin,
+                          int64_t row_end) {
+  const int n = B * B;
+  float* vals = (float*)malloc((size_t)n * sizeof(float));
+  uint64_t* idx = (uint64_t*)malloc((size_t)n * sizeof(uint64_t));
+  int* cds = (int*)malloc((size_t)n * sizeof(int));
+  orc_opts plain = *o;
+  plain.hadamard = 0;
+  for (int64_t br = row_begin / B; br < row_end / B; ++br) {
+    for (int64_t bc = 0; bc < cols / B; ++bc) {
+      for (int i = 0; i < B; ++i)
+        for (int j = 0; j < B; ++j) {
+          int64_t r = br * B + i, c = bc * B + j;
+          vals[i * B + j] = widen(x, dtype, r * ld + c);
+          idx[i * B + j] = (uint64_t)(r * cols + c);
+        }
+      uint8_t s = quantize_block(vals, idx, n, &plain, cds);
+      scales[br * (cols / B) + bc] = s;
+      if (scales_t) scales_t[bc * (rows / B) + br] = s;
+      for (int i = 0; i < B; ++i)
+        for (int j = 0; j < B; ++j) {
+          int64_t r = br * B + i, c = bc * B + j;
+          put_nibble(codes, r * cols + c, cds[i * B + j]);
+          if (codes_t) put_nibble(codes_t, c * rows + r, cds[i * B + j]);
+        }
+    }
+  }
+  free(vals);
+  free(idx);
+  free(cds);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------------------------ */
 /* Dequantize: value = E2M1(code) * 2^(byte - 127) in fp32 [P3 "Why FP4 ...": P * S].        */
 /* Optional inverse rotation per 32-block along a row: (1/32) * D * H.                        */
 /* ------------------------------------------------------------------------------------------ */

@@ -71,6 +71,8 @@ def lib():
         L.orc_e2m1_decode.restype = ctypes.c_float
         L.orc_e2m1_magnitude.argtypes = [i32]
         L.orc_e2m1_magnitude.restype = ctypes.c_float
+        L.orc_quantize_2d_block.argtypes = [vp, i32, i64, i64, i64, i32, ctypes.POINTER(_Opts), vp,
+                                            vp, vp, vp, i64, i64]
         L.orc_fp8_magnitude.argtypes = [i32, i32]
         L.orc_fp8_magnitude.restype = ctypes.c_double
         L.orc_fp8_decode.argtypes = [i32, i32]
@@ -210,6 +212,42 @@ def quantize_2d(x: np.ndarray, scale_rule: int = SCALE_CEIL, round_mode: int = R
                                 _ptr(codes), _ptr(scales), _ptr(codes_t), _ptr(scales_t), r0, r1,
                                 int(nthreads))
     return codes, scales, codes_t, scales_t
+
+
+def quantize_2d_block(x: np.ndarray, block: int, scale_rule: int = SCALE_CEIL,
+                      round_mode: int = ROUND_RNE, seed: int = 0, row_range=None):
+    """BxB quantize (block 8, 32 or 64): codes [rows][cols/2], scales [rows/B][cols/B], codes_t
+    [cols][rows/2], scales_t [cols/B][rows/B]."""
+    dt, ld = _src(x)
+    rows, cols = x.shape
+    B = int(block)
+    if B not in (8, 32, 64) or rows % B or cols % B:
+        raise ValueError("block must be 8, 32 or 64 and divide both dimensions")
+    codes = np.zeros((rows, cols // 2), dtype=np.uint8)
+    scales = np.zeros((rows // B, cols // B), dtype=np.uint8)
+    codes_t = np.zeros((cols, rows // 2), dtype=np.uint8)
+    scales_t = np.zeros((cols // B, rows // B), dtype=np.uint8)
+    r0, r1 = (0, rows) if row_range is None else row_range
+    o = _opts(scale_rule, round_mode, 0, 0, seed)
+    lib().orc_quantize_2d_block(_ptr(x), dt, rows, cols, ld, B, ctypes.byref(o), _ptr(codes),
+                                _ptr(scales), _ptr(codes_t), _ptr(scales_t), r0, r1)
+    return codes, scales, codes_t, scales_t
+
+
+def scale_mismatch_map(x: np.ndarray, scale_rule: int = SCALE_FLOOR) -> np.ndarray:
+    """Scale-difference map of 1x32 blocking ("Stable FP4 Training via Transposition-Invariant
+    Block Quantization", "The aha: transposition scrambles the blocks", Figure 1): for every
+    element, the scale exponent of its block along the row (how X enters the forward product)
+    minus that of its block down the column (how X enters the transposed product), as int8;
+    -128 where either block's maximum is not finite."""
+    rows, cols = x.shape
+    _, s_row = quantize(x, axis=1, scale_rule=scale_rule)
+    _, s_col = quantize(x, axis=0, scale_rule=scale_rule)
+    er = np.repeat(s_row.astype(np.int32), 32, axis=1)          # [rows][cols]
+    ec = np.repeat(s_col.astype(np.int32), 32, axis=1).T        # [cols][rows] -> [rows][cols]
+    d = er - ec
+    d[(er == 255) | (ec == 255)] = -128
+    return d.astype(np.int8)
 
 
 def dequantize(codes: np.ndarray, scales: np.ndarray, rows: int, cols: int, block_rows: int = 1,
