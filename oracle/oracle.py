@@ -238,14 +238,14 @@ def scale_mismatch_map(x: np.ndarray, scale_rule: int = SCALE_FLOOR) -> np.ndarr
     """Scale-difference map of 1x32 blocking ("Stable FP4 Training via Transposition-Invariant
     Block Quantization", "The aha: transposition scrambles the blocks", Figure 1): for every
     element, the scale exponent of its block along the row (how X enters the forward product)
-    minus that of its block down the column (how X enters the transposed product), as int8;
-    -128 where either block's maximum is not finite."""
+    minus that of its block down the column (how X enters the transposed product), saturated
+    to [-127, 127] as int8; -128 where either block's maximum is not finite."""
     rows, cols = x.shape
     _, s_row = quantize(x, axis=1, scale_rule=scale_rule)
     _, s_col = quantize(x, axis=0, scale_rule=scale_rule)
     er = np.repeat(s_row.astype(np.int32), 32, axis=1)          # [rows][cols]
     ec = np.repeat(s_col.astype(np.int32), 32, axis=1).T        # [cols][rows] -> [rows][cols]
-    d = er - ec
+    d = np.clip(er - ec, -127, 127)
     d[(er == 255) | (ec == 255)] = -128
     return d.astype(np.int8)
 

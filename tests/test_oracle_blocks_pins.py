@@ -90,3 +90,13 @@ def test_mismatch_map_marks_non_finite_blocks(orc):
     # the row block (row 5, columns 32-63) and the column block (rows 0-31, column 40)
     assert np.all(m[5, 32:64] == -128) and np.all(m[0:32, 40] == -128)
     assert (m == -128).sum() == 32 + 32 - 1 and np.all(m[m != -128] == 0)
+
+
+def test_mismatch_map_saturates(orc):
+    """Exponent differences beyond the int8 range saturate at +-127."""
+    x = np.full((32, 32), 1e-30, dtype=np.float32)
+    x[0, 0] = 1e30   # in the block of row 0 and in the block of column 0
+    m = orc.scale_mismatch_map(x).astype(np.int32)
+    assert m[0, 0] == 0 and m[5, 5] == 0
+    assert m[0, 5] == 127     # row block huge, column block tiny
+    assert m[5, 0] == -127    # row block tiny, column block huge
