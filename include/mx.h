@@ -138,7 +138,9 @@ mx_status mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t row
 /* Block-scaled MXFP4 GEMMs [P2 abstract; P3 "The aha ..."; P4 abstract].
  * All three compute C[m][n] = 2^alpha_exp * sum_k A[m][k] * B[n][k] with both operands packed
  * K-major (codes [rows][K/2]) and fp32 accumulation. A scale granularity g of 1 means scales
- * [rows][K/32]; g = 32 means 2-D scales [rows/32][K/32] (from mx_quantize_2d). alpha_exp = -5
+ * [rows][K/32]; g = 32 means 2-D scales [rows/32][K/32] (from mx_quantize_2d); g = 64 means
+ * [rows/64][K/32] (64x64 tiles from mx_quantize_2d_blocks, each byte covering two 32-k blocks).
+ * The operand's row count must be a multiple of g. alpha_exp = -5
  * undoes the factor 32 of two unnormalised Hadamard rotations along K (the caller guarantees
  * both operands used the same sign_mask); otherwise 0. out_dtype MX_BF16 (round to nearest
  * even) or MX_F32; ldc >= the output row length, in elements.
@@ -209,6 +211,36 @@ mx_status mx_quantize_mxfp8(const void* x, int32_t dtype, int64_t rows, int64_t 
 mx_status mx_gemm_mxfp8(const uint8_t* aq, const uint8_t* as, int32_t afmt, const uint8_t* bq,
                         const uint8_t* bs, int32_t bfmt, int64_t M, int64_t N, int64_t K,
                         int32_t alpha_exp, int32_t out_dtype, void* c, int64_t ldc, void* stream);
+
+/* Square tiles of other sizes [P3, "The fix ...": Table 4 compares 8x8, 32x32 and 64x64
+ * blocks, the smaller with more scale metadata]. As mx_quantize_2d with tile edge block = 8, 32
+ * or 64: one scale per tile from the tile maximum, every element rounded once and written to
+ * both code layouts (codes [rows][cols/2], codes_t [cols][rows/2], as for mx_quantize_2d).
+ * Scales: block = 8: scales [rows/8][cols/8], scales_t [cols/8][rows/8];
+ *         block = 32: exactly mx_quantize_2d;
+ *         block = 64: in the layout the GEMMs read with g = 64, scales [rows/64][cols/32] and
+ *                     scales_t [cols/64][rows/32], each tile's byte stored for both of its
+ *                     32-wide halves.
+ * 8x8 tiles cannot feed the block-scaled matrix cores, whose scale blocks are 32 elements along
+ * K; they are a quantization (and mismatch) format here. rows and cols must be multiples of
+ * max(block, 32); opts->hadamard must be 0. Alignment: x and source rows 16 bytes, codes and
+ * codes_t 16 bytes, scales and scales_t 4 bytes. Errors as for mx_quantize_2d, plus MX_ERR_ARG
+ * for another block. */
+mx_status mx_quantize_2d_blocks(const void* x, int32_t dtype, int64_t rows, int64_t cols,
+                                int64_t ld, int32_t block, const mx_quant_opts* opts,
+                                uint8_t* codes, uint8_t* scales, uint8_t* codes_t,
+                                uint8_t* scales_t, void* stream);
+
+/* Scale-difference map of 1x32 blocking [P3, "The aha: transposition scrambles the blocks",
+ * Figure 1]: map[r][c] = e_row - e_col, where e_row is the scale exponent (scale_rule, as for
+ * mx_quantize) of the 1x32 block along row r that holds element (r, c), how X enters the forward
+ * product, and e_col that of the 1x32 block down column c, how X enters the transposed product.
+ * int8, saturated to [-127, 127]; -128 where either block's maximum is not finite. With 32x32
+ * tiles the two exponents are one and the same, so the map of that quantizer is zero.
+ * x: [rows][ld] bf16 or fp32, rows and cols multiples of 32; map [rows][cols] contiguous, 8-byte
+ * aligned. Errors: MX_ERR_SHAPE, MX_ERR_ARG (dtype, scale_rule, alignment), MX_ERR_NULL. */
+mx_status mx_scale_mismatch_map(const void* x, int32_t dtype, int64_t rows, int64_t cols,
+                                int64_t ld, int32_t scale_rule, int8_t* map, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* mx_status_string(int32_t status);

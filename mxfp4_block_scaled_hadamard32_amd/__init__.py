@@ -10,6 +10,8 @@ in the library's HIP kernels.
   mx_dequantize   codes * 2^(scale-127), optional inverse rotation
   mx_gemm_fprop / mx_gemm_dgrad / mx_gemm_wgrad   block-scaled MXFP4 GEMMs, fp32 accumulate
   mx_gemm_fprop_quant   Fprop whose output tile is quantized (1x32 along N) in the epilogue
+  mx_quantize_2d_blocks   8x8, 32x32 or 64x64 tiles (64x64 scales in the GEMM layout, g = 64)
+  mx_scale_mismatch_map   per-element scale exponent of the row block minus the column block
   mx_quantize_mxfp8 / mx_gemm_mxfp8   MXFP8 (E4M3 / E5M2 elements, the same E8M0 block scales)
                   quantize and block-scaled GEMM, for the query / key projections
 """
@@ -24,7 +26,8 @@ from ._lib import (MX_BF16, MX_E4M3, MX_E5M2, MX_F32, MX_ROUND_RNE, MX_ROUND_SR,
                    MX_SCALE_FLOOR, MxError, check, lib, mx_quant_opts)
 
 __all__ = ["mx_quantize", "mx_quantize_2d", "mx_dequantize", "mx_gemm_fprop", "mx_gemm_dgrad",
-           "mx_gemm_wgrad", "mx_gemm_fprop_quant", "mx_quantize_mxfp8", "mx_gemm_mxfp8", "MxError",
+           "mx_gemm_wgrad", "mx_gemm_fprop_quant", "mx_quantize_mxfp8", "mx_gemm_mxfp8", "mx_quantize_2d_blocks",
+           "mx_scale_mismatch_map", "MxError",
            "MX_SCALE_FLOOR", "MX_SCALE_CEIL", "MX_ROUND_RNE", "MX_ROUND_SR", "MX_E4M3", "MX_E5M2",
            "lib"]
 
@@ -203,4 +206,42 @@ def mx_gemm_mxfp8(aq, as_, afmt, bq, bs, bfmt, alpha_exp=0, out_dtype=torch.bflo
     check(lib().mx_gemm_mxfp8(_ptr(aq), _ptr(as_), int(afmt), _ptr(bq), _ptr(bs), int(bfmt), M, N,
                               K, int(alpha_exp), code, _ptr(out), out.stride(0), _stream(stream)),
           "mx_gemm_mxfp8")
+    return out
+
+
+def mx_quantize_2d_blocks(x: torch.Tensor, block: int = 32, scale_rule: int = MX_SCALE_CEIL,
+                          round: int = MX_ROUND_RNE, seed: int = 0, transposed: bool = True,
+                          stream=None):
+    """BxB tiles (block 8, 32 or 64) -> (codes, scales, codes_t, scales_t); scales [rows/8]
+    [cols/8] for 8, [rows/32][cols/32] for 32, [rows/64][cols/32] (GEMM layout) for 64; the
+    transposed pair is None unless transposed."""
+    rows, cols, ld = _src(x)
+    dev = x.device
+    B = int(block)
+    shape_s = {8: (rows // 8, cols // 8), 32: (rows // 32, cols // 32), 64: (rows // 64, cols // 32)}
+    shape_st = {8: (cols // 8, rows // 8), 32: (cols // 32, rows // 32), 64: (cols // 64, rows // 32)}
+    if B not in shape_s:
+        raise ValueError("block must be 8, 32 or 64")
+    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty(shape_s[B], dtype=torch.uint8, device=dev)
+    codes_t = scales_t = None
+    if transposed:
+        codes_t = torch.empty((cols, rows // 2), dtype=torch.uint8, device=dev)
+        scales_t = torch.empty(shape_st[B], dtype=torch.uint8, device=dev)
+    o = _opts(scale_rule, round, 0, 0, seed)
+    check(lib().mx_quantize_2d_blocks(_ptr(x), _dtype_code(x), rows, cols, ld, B, ctypes.byref(o),
+                                      _ptr(codes), _ptr(scales), _ptr(codes_t), _ptr(scales_t),
+                                      _stream(stream)), "mx_quantize_2d_blocks")
+    return codes, scales, codes_t, scales_t
+
+
+def mx_scale_mismatch_map(x: torch.Tensor, scale_rule: int = MX_SCALE_FLOOR, out=None,
+                          stream=None) -> torch.Tensor:
+    """int8 [rows][cols]: scale exponent of each element's 1x32 row block minus that of its 1x32
+    column block (saturated; -128 for non-finite blocks)."""
+    rows, cols, ld = _src(x)
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.int8, device=x.device)
+    check(lib().mx_scale_mismatch_map(_ptr(x), _dtype_code(x), rows, cols, ld, int(scale_rule),
+                                      _ptr(out), _stream(stream)), "mx_scale_mismatch_map")
     return out

@@ -59,9 +59,12 @@ def lib() -> ctypes.CDLL:
     L.mx_quantize_mxfp8.argtypes = [vp, i32, i64, i64, i64, i32, i32, ctypes.POINTER(mx_quant_opts),
                                     vp, vp, vp]
     L.mx_gemm_mxfp8.argtypes = [vp, vp, i32, vp, vp, i32, i64, i64, i64, i32, i32, vp, i64, vp]
+    L.mx_quantize_2d_blocks.argtypes = [vp, i32, i64, i64, i64, i32, ctypes.POINTER(mx_quant_opts),
+                                        vp, vp, vp, vp, vp]
+    L.mx_scale_mismatch_map.argtypes = [vp, i32, i64, i64, i64, i32, vp, vp]
     for name in ("mx_quantize", "mx_quantize_2d", "mx_dequantize", "mx_gemm_fprop",
                  "mx_gemm_dgrad", "mx_gemm_wgrad", "mx_gemm_fprop_quant", "mx_quantize_mxfp8",
-                 "mx_gemm_mxfp8"):
+                 "mx_gemm_mxfp8", "mx_quantize_2d_blocks", "mx_scale_mismatch_map"):
         getattr(L, name).restype = ctypes.c_int
     L.mx_status_string.argtypes = [i32]
     L.mx_status_string.restype = ctypes.c_char_p

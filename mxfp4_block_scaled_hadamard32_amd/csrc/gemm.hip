@@ -902,7 +902,7 @@ hipError_t mx_launch_gemm(const GemmArgs& g) {
   // buffer offsets are 32-bit: one 256-row operand tile must stay below 2 GiB
   if ((int64_t)kBM * (g.K / 2) >= (int64_t)1 << 31) return hipErrorInvalidValue;
   const float alpha_f = __builtin_bit_cast(float, (uint32_t)(g.alpha + 127) << 23);
-  const int lga = g.ga == 32 ? 5 : 0, lgb = g.gb == 32 ? 5 : 0;
+  const int lga = g.ga == 64 ? 6 : g.ga == 32 ? 5 : 0, lgb = g.gb == 64 ? 6 : g.gb == 32 ? 5 : 0;
   const dim3 grid((unsigned)(nbm * nbn));
   // loads of a step issued during sub-steps 3, 0, 1 (the rest during sub-step 2): as early as
   // the at-most-one-load-per-MFMA-pair rule allows
@@ -931,7 +931,7 @@ hipError_t mx_launch_gemm_quant(const GemmArgs& g, const GemmQuantOut& q) {
   if ((int64_t)kBM * (g.K / 2) >= (int64_t)1 << 31) return hipErrorInvalidValue;
   if (g.K <= 0 || g.K % kBK != 0) return hipErrorInvalidValue;
   const float alpha_f = __builtin_bit_cast(float, (uint32_t)(g.alpha + 127) << 23);
-  const int lga = g.ga == 32 ? 5 : 0, lgb = g.gb == 32 ? 5 : 0;
+  const int lga = g.ga == 64 ? 6 : g.ga == 32 ? 5 : 0, lgb = g.gb == 64 ? 6 : g.gb == 32 ? 5 : 0;
   const dim3 grid((unsigned)(nbm * nbn));
   constexpr int kS3 = kStreamWaves == 4 ? 8 : 4, kS0 = kStreamWaves == 4 ? 8 : 4;
   constexpr int kS1 = kStreamWaves == 4 ? 1 : 2;

@@ -11,6 +11,9 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 mx_status launch_status(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_LAUNCH; }
 
+// scale row granularity of a GEMM operand: per row, per 32x32 tile or per 64x64 tile
+bool granularity_ok(int32_t g) { return g == 1 || g == 32 || g == 64; }
+
 mx_status check_opts(const mx_quant_opts* o) {
   if (!o) return MX_ERR_NULL;
   if (o->scale_rule != MX_SCALE_FLOOR && o->scale_rule != MX_SCALE_CEIL) return MX_ERR_ARG;
@@ -35,7 +38,8 @@ mx_status gemm(const uint8_t* a, const uint8_t* as, int32_t ga, const uint8_t* b
   if (M < 0 || N < 0 || K < 0) return MX_ERR_SHAPE;
   if (M % 32 || N % 32 || K % 32) return MX_ERR_SHAPE;
   if (ldc < N || ldc % 8 != 0) return MX_ERR_SHAPE;
-  if ((ga != 1 && ga != 32) || (gb != 1 && gb != 32)) return MX_ERR_ARG;
+  if (!granularity_ok(ga) || !granularity_ok(gb)) return MX_ERR_ARG;
+  if (M % ga || N % gb) return MX_ERR_SHAPE;
   if (out_dtype != MX_F32 && out_dtype != MX_BF16) return MX_ERR_ARG;
   if (alpha_exp < -126 || alpha_exp > 127) return MX_ERR_ARG;
   if (M == 0 || N == 0) return MX_OK;
@@ -113,7 +117,8 @@ mx_status mx_gemm_fprop_quant(const uint8_t* xq, const uint8_t* xs, int32_t gx, 
   if (s != MX_OK) return s;
   if (T < 0 || N < 0 || K < 0) return MX_ERR_SHAPE;
   if (T % 32 || N % 32 || K % 32) return MX_ERR_SHAPE;
-  if ((gx != 1 && gx != 32) || (gw != 1 && gw != 32)) return MX_ERR_ARG;
+  if (!granularity_ok(gx) || !granularity_ok(gw)) return MX_ERR_ARG;
+  if (T % gx || N % gw) return MX_ERR_SHAPE;
   if (alpha_exp < -126 || alpha_exp > 127) return MX_ERR_ARG;
   if (T == 0 || N == 0) return MX_OK;
   if (K == 0 || K % 128 != 0) return MX_ERR_UNSUPPORTED;  // the streaming kernels only
@@ -181,6 +186,41 @@ mx_status mx_gemm_mxfp8(const uint8_t* aq, const uint8_t* as, int32_t afmt, cons
   if (!aq || !as || !bq || !bs) return MX_ERR_NULL;
   if (!aligned(aq, 16) || !aligned(bq, 16)) return MX_ERR_ARG;
   return launch_status(mx_launch_gemm_fp8(g, afmt, bfmt));
+}
+
+mx_status mx_quantize_2d_blocks(const void* x, int32_t dtype, int64_t rows, int64_t cols,
+                                int64_t ld, int32_t block, const mx_quant_opts* opts,
+                                uint8_t* codes, uint8_t* scales, uint8_t* codes_t,
+                                uint8_t* scales_t, void* stream) {
+  mx_status s = check_opts(opts);
+  if (s != MX_OK) return s;
+  if (block != 8 && block != 32 && block != 64) return MX_ERR_ARG;
+  if (opts->hadamard) return MX_ERR_UNSUPPORTED;
+  if ((s = check_source(x, dtype, rows, cols, ld)) != MX_OK) return s;
+  const int64_t unit = block > 32 ? block : 32;
+  if (rows % unit != 0 || cols % unit != 0) return MX_ERR_SHAPE;
+  if ((codes_t == nullptr) != (scales_t == nullptr)) return MX_ERR_NULL;
+  if (rows == 0 || cols == 0) return MX_OK;
+  if (!x || !codes || !scales) return MX_ERR_NULL;
+  if (!aligned(codes, 16) || (codes_t && !aligned(codes_t, 16))) return MX_ERR_ARG;
+  if (!aligned(scales, 4) || (scales_t && !aligned(scales_t, 4))) return MX_ERR_ARG;
+  QuantArgs a{x, dtype == MX_BF16, rows, cols, ld, 1, opts->scale_rule == MX_SCALE_CEIL,
+              opts->round == MX_ROUND_SR, false, 0u, opts->seed, codes, scales, codes_t,
+              scales_t, stream};
+  return launch_status(mx_launch_quantize_2d_blocks(a, block));
+}
+
+mx_status mx_scale_mismatch_map(const void* x, int32_t dtype, int64_t rows, int64_t cols,
+                                int64_t ld, int32_t scale_rule, int8_t* map, void* stream) {
+  if (scale_rule != MX_SCALE_FLOOR && scale_rule != MX_SCALE_CEIL) return MX_ERR_ARG;
+  mx_status s = check_source(x, dtype, rows, cols, ld);
+  if (s != MX_OK) return s;
+  if (rows % 32 != 0 || cols % 32 != 0) return MX_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return MX_OK;
+  if (!x || !map) return MX_ERR_NULL;
+  if (!aligned(map, 8)) return MX_ERR_ARG;
+  return launch_status(mx_launch_scale_mismatch(x, dtype == MX_BF16, rows, cols, ld,
+                                                scale_rule == MX_SCALE_CEIL, map, stream));
 }
 
 const char* mx_status_string(int32_t status) {

@@ -25,6 +25,13 @@ hipError_t mx_launch_quantize_2d(const QuantArgs& a);
 // MXFP8 1x32 quantize (fmt 0 = E4M3, 1 = E5M2): codes one byte per element,
 // axis 1: [rows][cols], axis 0: [cols][rows]; scales as for MXFP4
 hipError_t mx_launch_quantize_fp8(const QuantArgs& a, int fmt);
+// B x B tiles (block 8, 32 or 64; rows and cols multiples of max(block, 32)); for 64 the scales
+// are in the GEMM layout [rows/64][cols/32] / [cols/64][rows/32] (each byte twice)
+hipError_t mx_launch_quantize_2d_blocks(const QuantArgs& a, int block);
+// map[r][c] = scale byte of the row block of (r, c) minus that of its column block (int8,
+// saturated; -128 for a non-finite block); rows, cols multiples of 32
+hipError_t mx_launch_scale_mismatch(const void* x, bool bf16, int64_t rows, int64_t cols,
+                                    int64_t ld, bool ceil, int8_t* map, void* stream);
 hipError_t mx_launch_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows,
                                 int64_t cols, int block_rows, int inv_had, uint32_t sign_mask,
                                 float* out, void* stream);

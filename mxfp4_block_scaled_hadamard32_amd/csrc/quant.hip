@@ -28,6 +28,7 @@ namespace {
 using namespace mxd;
 
 constexpr int kThreads = 256;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kRowChunksPerThread = 2;
 
 template <bool BF16>
@@ -348,13 +349,192 @@ __global__ __launch_bounds__(kThreads) void quant_2d_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------
+// B x B tiles, B = 8 or 64 [P3 "The fix ...", Table 4: the 32x32 rule with smaller and larger
+// tiles]. A workgroup owns 256 rows x 256 columns, as the 32x32 kernel; pass p of wave w covers
+// the 64x64 sub-tile t = 4p + w (sub-row t / 4, sub-column t % 4), where lane l holds the 8x8
+// patch at rows 8 (l / 8), columns 8 (l % 8). With B = 8 a patch is a tile (its maximum stays in
+// the lane); with B = 64 the sub-tile is a tile, its maximum reduced over the wave. Codes are
+// assembled in LDS in both layouts and leave as whole 128-byte rows. Scales: B = 8, [rows/8]
+// [cols/8] and [cols/8][rows/8]; B = 64, the GEMM layout [rows/64][cols/32] and
+// [cols/64][rows/32], each tile's byte stored for both of its 32-wide halves. rows and cols
+// are multiples of max(B, 32).
+// ---------------------------------------------------------------------------------------------
+template <int B, bool BF16, bool SR, bool CEIL>
+__global__ __launch_bounds__(kThreads) void quant_2d_var_kernel(
+    const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, uint64_t seed,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, uint8_t* __restrict__ codes_t,
+    uint8_t* __restrict__ scales_t, int64_t n_ct) {
+  static_assert(B == 8 || B == 64, "8x8 or 64x64 tiles");
+  constexpr int NS = k2dTile / B;  // tiles per edge of the workgroup tile
+  __shared__ __attribute__((aligned(16))) uint8_t rtile[k2dTile * k2dStride];  // [row][col/2]
+  __shared__ __attribute__((aligned(16))) uint8_t ttile[k2dTile * k2dStride];  // [col][row/2]
+  __shared__ __attribute__((aligned(16))) uint8_t stile[NS * NS];               // [tr][tc]
+  const int64_t rt = blockIdx.x / n_ct, ct = blockIdx.x - rt * n_ct;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int pr = lane >> 3, pc = lane & 7;
+  const int64_t rtile0 = rt * k2dTile, ctile0 = ct * k2dTile;
+  const int nr = (int)min((int64_t)k2dTile, rows - rtile0);  // multiple of 32 (of 64 for B = 64)
+  const int nc = (int)min((int64_t)k2dTile, cols - ctile0);
+
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int t = 4 * pass + wave, sr = t >> 2, sc = t & 3;
+    const int rl0 = 64 * sr + 8 * pr, cl0 = 64 * sc + 8 * pc;  // patch origin in the tile
+    if (B == 64) {
+      if (64 * sr >= nr || 64 * sc >= nc) continue;  // whole 64x64 tiles, uniform per wave
+    } else if (rl0 >= nr || cl0 >= nc) {
+      continue;                                       // whole 8x8 tiles
+    }
+    const int64_t r0 = rtile0 + rl0, c0 = ctile0 + cl0;
+    float p[8][8];
+    load_patch<BF16>(x, ld, r0, c0, p);
+
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) m = max(m, abs_bits(p[j][k]));
+    if (B == 64) {
+      m = max(m, dpp_u32<kQuadXor1>(m));
+      m = max(m, dpp_u32<kQuadXor2>(m));
+      m = max(m, dpp_u32<kRowRor4>(m));
+      m = max(m, dpp_u32<kRowRor8>(m));
+      m = max(m, (uint32_t)__shfl_xor((int)m, 16));
+      m = max(m, (uint32_t)__shfl_xor((int)m, 32));
+    }
+    const uint32_t sb = scale_byte<CEIL>(m);
+
+    uint32_t R[8];  // R[j] = codes of patch row j (nibble k = column k)
+    if (sb == 0xFFu) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) R[j] = 0;
+    } else {
+      const float inv = inv_scale_from_byte(sb);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) p[j][k] = p[j][k] * inv;
+        if (SR) {
+          uint32_t rw[8];
+          sr_rand8((uint64_t)((r0 + j) * cols + c0) >> 3, seed, rw);
+          R[j] = sr_pack8(p[j], rw);
+        } else {
+          R[j] = cvt_rne_pack8(p[j]);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      *reinterpret_cast<uint32_t*>(rtile + (rl0 + j) * k2dStride + cl0 / 2) = R[j];
+    transpose_nibbles8x8(R);  // R[k] = codes of patch column k (nibble j = row j)
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      *reinterpret_cast<uint32_t*>(ttile + (cl0 + k) * k2dStride + rl0 / 2) = R[k];
+    if (B == 8) stile[(rl0 / 8) * NS + cl0 / 8] = (uint8_t)sb;
+    else if (lane == 0) stile[sr * NS + sc] = (uint8_t)sb;
+  }
+  __syncthreads();
+
+  // codes: 8 lanes per row (column) of the tile, 16 bytes (32 codes) each
+  const int64_t cols2 = cols / 2, rows2 = rows / 2;
+  const int seg = threadIdx.x & 7;
+#pragma unroll
+  for (int round = 0; round < k2dTile * 8 / kThreads; ++round) {
+    const int i = round * (kThreads / 8) + (threadIdx.x >> 3);
+    if (i < nr && 32 * seg < nc)
+      __builtin_nontemporal_store(
+          *reinterpret_cast<const u32x4*>(rtile + i * k2dStride + 16 * seg),
+          reinterpret_cast<u32x4*>(codes + (rtile0 + i) * cols2 + ctile0 / 2 + 16 * seg));
+    if (codes_t && i < nc && 32 * seg < nr)
+      __builtin_nontemporal_store(
+          *reinterpret_cast<const u32x4*>(ttile + i * k2dStride + 16 * seg),
+          reinterpret_cast<u32x4*>(codes_t + (ctile0 + i) * rows2 + rtile0 / 2 + 16 * seg));
+  }
+  if (B == 8) {
+    // thread t: scale row (column) t / 8 of the tile, 4 bytes (32 source columns) at t % 8
+    const int a = threadIdx.x >> 3, b4 = 4 * (threadIdx.x & 7);
+    if (8 * a < nr && 8 * b4 < nc)
+      *reinterpret_cast<uint32_t*>(scales + (rtile0 / 8 + a) * (cols / 8) + ctile0 / 8 + b4) =
+          *reinterpret_cast<const uint32_t*>(stile + a * NS + b4);
+    if (scales_t && 8 * a < nc && 8 * b4 < nr) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w |= (uint32_t)stile[(b4 + i) * NS + a] << (8 * i);
+      *reinterpret_cast<uint32_t*>(scales_t + (ctile0 / 8 + a) * (rows / 8) + rtile0 / 8 + b4) = w;
+    }
+  } else if (threadIdx.x < NS * NS) {
+    const int i = threadIdx.x / NS, j = threadIdx.x % NS;
+    if (64 * i < nr && 64 * j < nc) {
+      const uint16_t v = (uint16_t)(stile[i * NS + j] * 0x0101u);
+      *reinterpret_cast<uint16_t*>(scales + (rtile0 / 64 + i) * (cols / 32) + ctile0 / 32 + 2 * j) = v;
+      if (scales_t)
+        *reinterpret_cast<uint16_t*>(scales_t + (ctile0 / 64 + j) * (rows / 32) + rtile0 / 32 + 2 * i) = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// 1D scale-difference map [P3 "The aha: transposition scrambles the blocks", Figure 1]: for
+// every element, the scale exponent of its 1x32 block along the row minus that of its 1x32
+// block down the column, saturated to [-127, 127] (-128 where a block maximum is not finite).
+// Wave unit u = 4 blockIdx + wave covers row block u / ncg (32 rows) and 128-column group
+// u % ncg, laid out as in the 32x32 kernel: lane = 16 tile + 4 cg + q holds the 8x8 patch at
+// rows 8q, columns 8 (4 tile + cg). Column maxima reduce over the quad (q), row maxima over the
+// four column groups of the tile (DPP row rotations by 4 and 8).
+// ---------------------------------------------------------------------------------------------
+template <bool BF16, bool CEIL>
+__global__ __launch_bounds__(kThreads) void mismatch_map_kernel(
+    const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, u32x2* __restrict__ map,
+    int64_t nunits, int64_t ncg) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t u = (int64_t)blockIdx.x * 4 + wave;
+  if (u >= nunits) return;  // uniform per wave
+  const int q = lane & 3, cgl = lane >> 2;
+  const int64_t rb = u / ncg, g = u - rb * ncg;
+  const int64_t r0 = rb * 32 + 8 * q, c0 = g * 128 + 8 * cgl;
+  if (c0 >= cols) return;  // whole 32-column tiles (cols % 32 == 0), i.e. whole DPP rows
+  float p[8][8];
+  load_patch<BF16>(x, ld, r0, c0, p);
+  uint32_t sc[8], sr[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = max(m, abs_bits(p[j][k]));
+    m = max(m, dpp_u32<kQuadXor1>(m));
+    m = max(m, dpp_u32<kQuadXor2>(m));
+    sc[k] = scale_byte<CEIL>(m);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) m = max(m, abs_bits(p[j][k]));
+    m = max(m, dpp_u32<kRowRor4>(m));
+    m = max(m, dpp_u32<kRowRor8>(m));
+    sr[j] = scale_byte<CEIL>(m);
+  }
+  const int64_t cpr = cols / 8;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      int d = (int)sr[j] - (int)sc[k];
+      d = min(max(d, -127), 127);
+      if (sr[j] == 0xFFu || sc[k] == 0xFFu) d = -128;
+      w[k >> 2] |= ((uint32_t)d & 0xFFu) << (8 * (k & 3));
+    }
+    __builtin_nontemporal_store(u32x2{w[0], w[1]}, map + (r0 + j) * cpr + c0 / 8);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // MXFP8 [P3 "The fix, and its supporting cast": queries and keys in MXFP8]: the same block
 // structure with one code byte per element (E4M3 or E5M2). Along rows a lane's 8 codes are 8
 // consecutive output bytes; down the columns a lane's 8 codes of one column go to an LDS tile
 // of 256 bytes per column (the tile's 256 rows), which leaves as whole 256-byte pieces.
 // ---------------------------------------------------------------------------------------------
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
 template <int FMT, bool BF16, bool HAD, bool SR, bool CEIL>
 __global__ __launch_bounds__(kThreads) void quant_rows_fp8_kernel(
     const void* __restrict__ x, int64_t nchunks, int64_t cpr, int64_t ld, int contiguous,
@@ -583,6 +763,34 @@ hipError_t pick_2d(const QuantArgs& a) {
   return a.ceil ? launch_2d<BF16, false, true>(a) : launch_2d<BF16, false, false>(a);
 }
 
+template <int B, bool BF16, bool SR, bool CEIL>
+hipError_t launch_2d_var(const QuantArgs& a) {
+  const int64_t n_rt = (a.rows + k2dTile - 1) / k2dTile, n_ct = (a.cols + k2dTile - 1) / k2dTile;
+  if (n_rt * n_ct > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((quant_2d_var_kernel<B, BF16, SR, CEIL>), dim3((unsigned)(n_rt * n_ct)),
+                     dim3(kThreads), 0, (hipStream_t)a.stream, a.x, a.rows, a.cols, a.ld, a.seed,
+                     a.codes, a.scales, a.codes_t, a.scales_t, n_ct);
+  return hipGetLastError();
+}
+
+template <int B, bool BF16>
+hipError_t pick_2d_var(const QuantArgs& a) {
+  if (a.sr) return a.ceil ? launch_2d_var<B, BF16, true, true>(a) : launch_2d_var<B, BF16, true, false>(a);
+  return a.ceil ? launch_2d_var<B, BF16, false, true>(a) : launch_2d_var<B, BF16, false, false>(a);
+}
+
+template <bool BF16, bool CEIL>
+hipError_t launch_mismatch(const void* x, int64_t rows, int64_t cols, int64_t ld, int8_t* map,
+                           void* stream) {
+  const int64_t ncg = (cols + 127) / 128, nunits = (rows / 32) * ncg;
+  const int64_t nblocks = (nunits + 3) / 4;
+  if (nblocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((mismatch_map_kernel<BF16, CEIL>), dim3((unsigned)nblocks), dim3(kThreads), 0,
+                     (hipStream_t)stream, x, rows, cols, ld, reinterpret_cast<u32x2*>(map), nunits,
+                     ncg);
+  return hipGetLastError();
+}
+
 template <int FMT, bool BF16, bool HAD, bool SR, bool CEIL>
 hipError_t launch_fp8(const QuantArgs& a) {
   if (a.axis == 1) {
@@ -643,4 +851,18 @@ hipError_t mx_launch_dequantize(const uint8_t* codes, const uint8_t* scales, int
 
 hipError_t mx_launch_quantize_fp8(const QuantArgs& a, int fmt) {
   return fmt == 0 ? pick_fp8<0>(a) : pick_fp8<1>(a);
+}
+
+hipError_t mx_launch_quantize_2d_blocks(const QuantArgs& a, int block) {
+  if (block == 32) return mx_launch_quantize_2d(a);
+  if (block == 8) return a.bf16 ? pick_2d_var<8, true>(a) : pick_2d_var<8, false>(a);
+  return a.bf16 ? pick_2d_var<64, true>(a) : pick_2d_var<64, false>(a);
+}
+
+hipError_t mx_launch_scale_mismatch(const void* x, bool bf16, int64_t rows, int64_t cols,
+                                    int64_t ld, bool ceil, int8_t* map, void* stream) {
+  if (bf16) return ceil ? launch_mismatch<true, true>(x, rows, cols, ld, map, stream)
+                        : launch_mismatch<true, false>(x, rows, cols, ld, map, stream);
+  return ceil ? launch_mismatch<false, true>(x, rows, cols, ld, map, stream)
+              : launch_mismatch<false, false>(x, rows, cols, ld, map, stream);
 }

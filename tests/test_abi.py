@@ -166,3 +166,40 @@ def test_gemm_mxfp8_argument_errors(L):
     assert call(a=None) == m.MX_ERR_NULL
     assert call(c=ctypes.c_void_p(0x10008)) == m.MX_ERR_ARG
     assert call(N=0, c=None) == m.MX_OK
+
+
+def test_quantize_2d_blocks_argument_errors(L):
+    from mxfp4_block_scaled_hadamard32_amd import _lib as m
+    q = L.mx_quantize_2d_blocks
+
+    def call(rows=128, cols=128, ld=128, block=64, o=None, codes=FAKE, scales=FAKE, ct=None, st=None):
+        return q(FAKE, 1, rows, cols, ld, block, opts() if o is None else o, codes, scales, ct, st,
+                 None)
+    assert call(block=16) == m.MX_ERR_ARG
+    assert call(rows=96) == m.MX_ERR_SHAPE                 # 64x64 needs multiples of 64
+    assert call(block=8, cols=40, ld=48) == m.MX_ERR_SHAPE  # multiples of 32 even for 8x8
+    assert call(o=opts(hadamard=1)) == m.MX_ERR_UNSUPPORTED
+    assert call(ct=FAKE) == m.MX_ERR_NULL
+    assert call(scales=ctypes.c_void_p(0x10002)) == m.MX_ERR_ARG
+    assert call(codes=None) == m.MX_ERR_NULL
+    assert call(rows=0, codes=None, scales=None) == m.MX_OK
+
+
+def test_scale_mismatch_map_argument_errors(L):
+    from mxfp4_block_scaled_hadamard32_amd import _lib as m
+    f = L.mx_scale_mismatch_map
+    assert f(FAKE, 1, 64, 48, 48, 0, FAKE, None) == m.MX_ERR_SHAPE
+    assert f(FAKE, 1, 40, 64, 64, 0, FAKE, None) == m.MX_ERR_SHAPE
+    assert f(FAKE, 1, 64, 64, 64, 2, FAKE, None) == m.MX_ERR_ARG
+    assert f(FAKE, 3, 64, 64, 64, 0, FAKE, None) == m.MX_ERR_ARG
+    assert f(FAKE, 1, 64, 64, 64, 0, None, None) == m.MX_ERR_NULL
+    assert f(FAKE, 1, 64, 64, 64, 0, ctypes.c_void_p(0x10004), None) == m.MX_ERR_ARG
+    assert f(None, 1, 0, 64, 64, 0, None, None) == m.MX_OK
+
+
+def test_gemm_64_row_granularity_needs_whole_tiles(L):
+    from mxfp4_block_scaled_hadamard32_amd import _lib as m
+    g = L.mx_gemm_fprop
+    assert g(FAKE, FAKE, 64, FAKE, FAKE, 1, 96, 64, 64, 0, 1, FAKE, 64, None) == m.MX_ERR_SHAPE
+    assert g(FAKE, FAKE, 1, FAKE, FAKE, 64, 64, 96, 64, 0, 1, FAKE, 96, None) == m.MX_ERR_SHAPE
+    assert g(FAKE, FAKE, 16, FAKE, FAKE, 1, 64, 64, 64, 0, 1, FAKE, 64, None) == m.MX_ERR_ARG
