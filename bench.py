@@ -53,8 +53,8 @@ def parse():
     p.add_argument("--step-only", action="store_true",
                    help="skip the comparisons run after the timed steps (fused epilogue, linear "
                         "layer), so that a profile of the run holds the step's launches alone")
-    p.add_argument("--with-mxfp8", action="store_true",
-                   help="with --step-only, still run the MXFP8 attention-projection comparison")
+    p.add_argument("--with-variants", action="store_true",
+                   help="with --step-only, still run the MXFP8 and tile-size variant comparisons")
     p.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="no GPU work: turn the counter_collection.csv files of a FETCH_SIZE and "
                         "a WRITE_SIZE rocprofv3 pass over a --copy-calibration run into the "
@@ -304,6 +304,57 @@ def mxfp8_attention(mx, wl, torch, reps: int = 5):
     return res
 
 
+def block_variants(mx, wl, torch, reps: int = 5):
+    """Outside the timed step: the tile-size variants on the 2-D workload (W 14336x4096, X
+    8192x4096, bf16, ceil scale, RNE): 8x8, 32x32 and 64x64 quantization with both code layouts,
+    Fprop on W's 32x32 and 64x64 scales against 1x32, and the 1D scale-mismatch map of X with its
+    summary (the share of elements whose two 1D scales differ, and the mean |difference|)."""
+    d = wl.blocks_2d(device="cuda")
+    X, W = d["X"], d["W"]
+    N, K = W.shape
+    T = X.shape[0]
+
+    def timed(fn):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    res = {"blocks_workload": "2-D workload W 14336x4096 and X 8192x4096 bf16, ceil scale, RNE"}
+    ops = {}
+    for B in (8, 32, 64):
+        ops[B] = mx.mx_quantize_2d_blocks(W, block=B, scale_rule=1)
+        c, sc, ct, st = ops[B]
+        ms = timed(lambda: mx.mx_quantize_2d_blocks(W, block=B, scale_rule=1, codes=c, scales=sc,
+                                                    codes_t=ct, scales_t=st))
+        sbytes = sum(t.numel() for t in (ops[B][1], ops[B][3]))
+        gbs = (N * K * 3 + sbytes) / (ms * 1e-3) / 1e9  # bf16 in, both code layouts, scales
+        res[f"quant_2d_{B}x{B}_ms"] = round(ms, 4)
+        res[f"quant_2d_{B}x{B}_gbs"] = round(gbs, 1)
+    xq, xs = mx.mx_quantize(X, scale_rule=1)
+    w1q, w1s = mx.mx_quantize(W, scale_rule=1)
+    y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+    flops = 2.0 * T * N * K
+    for name, (wq, ws, g) in (("1x32", (w1q, w1s, 1)), ("32x32", (ops[32][0], ops[32][1], 32)),
+                              ("64x64", (ops[64][0], ops[64][1], 64))):
+        ms = timed(lambda: mx.mx_gemm_fprop(xq, xs, 1, wq, ws, g, out=y))
+        res[f"fprop_w_{name}_ms"] = round(ms, 4)
+        res[f"fprop_w_{name}_tflops"] = round(flops / (ms * 1e-3) / 1e12, 1)
+    m = mx.mx_scale_mismatch_map(X)
+    ms = timed(lambda: mx.mx_scale_mismatch_map(X, out=m))
+    res["mismatch_map_ms"] = round(ms, 4)
+    res["mismatch_map_gbs"] = round(T * K * 3 / (ms * 1e-3) / 1e9, 1)
+    mf = m.float()
+    res["mismatch_1d_share_nonzero"] = round(float((m != 0).float().mean()), 4)
+    res["mismatch_1d_mean_abs"] = round(float(mf.abs().mean()), 4)
+    return res
+
+
 COPY_BYTES = 1 << 30  # the --copy-calibration copy reads and writes 1 GiB
 
 
@@ -356,10 +407,10 @@ def write_traffic(fetch_csv: str, write_csv: str, workload: str):
     rec = {"gemm_sha": sha(GEMM_SRC), "fetch_factor": ff, "write_factor": wf,
            "command_fetch": ("rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch "
                              "-o run -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline "
-                             "--step-only --with-mxfp8 --copy-calibration"),
+                             "--step-only --with-variants --copy-calibration"),
            "command_write": ("rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write "
                              "-o run -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline "
-                             "--step-only --with-mxfp8 --copy-calibration")}
+                             "--step-only --with-variants --copy-calibration")}
     for name, M, Nn, Kk in (("fprop", T, N, K), ("dgrad", T, K, N), ("wgrad", N, K, T)):
         wgs = ((M + 255) // 256) * ((Nn + 255) // 256)
         hbm = gemm_value(fetch, wgs) * 1024.0 * ff + gemm_value(write, wgs) * 1024.0 * wf
@@ -458,8 +509,9 @@ def main():
     if not args.step_only:
         out["components"].update(fused_epilogue(layer, torch))
         out["components"].update(linear_layer(layer, torch))
-    if not args.step_only or args.with_mxfp8:
+    if not args.step_only or args.with_variants:
         out["components"].update(mxfp8_attention(mx, wl, torch))
+        out["components"].update(block_variants(mx, wl, torch))
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         cb = cpu_baseline(layer, args.cpu_sample_rows)

@@ -211,7 +211,7 @@ def mx_gemm_mxfp8(aq, as_, afmt, bq, bs, bfmt, alpha_exp=0, out_dtype=torch.bflo
 
 def mx_quantize_2d_blocks(x: torch.Tensor, block: int = 32, scale_rule: int = MX_SCALE_CEIL,
                           round: int = MX_ROUND_RNE, seed: int = 0, transposed: bool = True,
-                          stream=None):
+                          codes=None, scales=None, codes_t=None, scales_t=None, stream=None):
     """BxB tiles (block 8, 32 or 64) -> (codes, scales, codes_t, scales_t); scales [rows/8]
     [cols/8] for 8, [rows/32][cols/32] for 32, [rows/64][cols/32] (GEMM layout) for 64; the
     transposed pair is None unless transposed."""
@@ -222,12 +222,17 @@ def mx_quantize_2d_blocks(x: torch.Tensor, block: int = 32, scale_rule: int = MX
     shape_st = {8: (cols // 8, rows // 8), 32: (cols // 32, rows // 32), 64: (cols // 64, rows // 32)}
     if B not in shape_s:
         raise ValueError("block must be 8, 32 or 64")
-    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
-    scales = torch.empty(shape_s[B], dtype=torch.uint8, device=dev)
-    codes_t = scales_t = None
-    if transposed:
-        codes_t = torch.empty((cols, rows // 2), dtype=torch.uint8, device=dev)
-        scales_t = torch.empty(shape_st[B], dtype=torch.uint8, device=dev)
+    if codes is None:
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty(shape_s[B], dtype=torch.uint8, device=dev)
+    if not transposed:
+        codes_t = scales_t = None
+    else:
+        if codes_t is None:
+            codes_t = torch.empty((cols, rows // 2), dtype=torch.uint8, device=dev)
+        if scales_t is None:
+            scales_t = torch.empty(shape_st[B], dtype=torch.uint8, device=dev)
     o = _opts(scale_rule, round, 0, 0, seed)
     check(lib().mx_quantize_2d_blocks(_ptr(x), _dtype_code(x), rows, cols, ld, B, ctypes.byref(o),
                                       _ptr(codes), _ptr(scales), _ptr(codes_t), _ptr(scales_t),
