@@ -27,9 +27,11 @@ constexpr int kQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
 constexpr int kRowRor4 = 0x124;  // rotate right by 4 within a row of 16 lanes
 constexpr int kRowRor8 = 0x128;  // rotate right by 8 within a row of 16 lanes
 
+// Every caller exchanges inside whole quads or whole 16-lane rows of active lanes, so no source
+// lane is inactive; bound_ctrl lets the compiler fold the move into the consuming add or max.
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
 }
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
@@ -112,7 +114,9 @@ __device__ __forceinline__ float inv_scale_from_byte(uint32_t byte) {
 //      identity for |v| >= 1 (there the 22 bits below E2M1's mantissa bit are all of f) and
 //      turns f * 2^22 into ceil(f * 2^22) below 1 (grid step 1/2); a value just under a grid
 //      point that rounds up onto it is then rounded up by the converter for every r, as the
-//      rule does. |v| * 2^23 and the products are exact fp32 operations.
+//      rule does. |v| * 2^23 and the products are exact fp32 operations. The converter divides
+//      its input by its scale operand, so ceil(|v| * 2^23) goes in with scale 2^23 (checked
+//      equal to the unit-scale conversion of the rounded value on 1M random value/word pairs).
 // ---------------------------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t cvt_rne_pack8(const float (&v)[8]) {
   uint32_t w = 0;
@@ -124,7 +128,7 @@ __device__ __forceinline__ uint32_t cvt_rne_pack8(const float (&v)[8]) {
 }
 
 // The converter writes the pair's codes to byte 0 (the first value in the low nibble); the
-// pair's second value is just the next register, its code is discarded, and the nibble is
+// pair's second value is a zero whose code is discarded, and the nibble is
 // placed by hand (the compiler does not carry the untouched bytes of the destination through
 // this builtin, so byte selection cannot accumulate a word). rw[k] = (~r_k << 16) | 0xFFFF.
 __device__ __forceinline__ uint32_t sr_pack8(const float (&v)[8], const uint32_t (&rw)[8]) {
@@ -132,9 +136,9 @@ __device__ __forceinline__ uint32_t sr_pack8(const float (&v)[8], const uint32_t
   uint32_t w = 0;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    const float up = __builtin_ceilf(fabsf(v[k]) * 8388608.0f) * 1.1920928955078125e-07f;
-    const f32x2_t pair = {__builtin_copysignf(up, v[k]), v[k < 7 ? k + 1 : k]};
-    const uint32_t code = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, pair, rw[k], 1.0f, 0);
+    const float up = __builtin_ceilf(fabsf(v[k]) * 8388608.0f);  // |v| up to 2^-23, times 2^23
+    const f32x2_t pair = {__builtin_copysignf(up, v[k]), 0.0f};
+    const uint32_t code = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, pair, rw[k], 8388608.0f, 0);
     w |= (code & 0xFu) << (4 * k);
   }
   return w;
@@ -151,8 +155,8 @@ __device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
   for (int round = 0; round < 10; ++round) {
     const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
     const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
-    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
-    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, 0x96);  // a^b^c
+    const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x96);
     c1 = (uint32_t)p1;
     c3 = (uint32_t)p0;
     c0 = n0;
