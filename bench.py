@@ -218,7 +218,8 @@ def fused_epilogue(layer, torch, reps: int = 5):
 
 def linear_layer(layer, torch, reps: int = 3):
     """Outside the timed step: forward + backward of the MXFP4 linear layer (autograd op, the
-    layer's quantization options on all three GEMMs) against the same op with every GEMM in bf16."""
+    layer's quantization options on all three GEMMs; and the 2-D tile recipe) against the same op
+    with every GEMM in bf16."""
     from mxfp4_block_scaled_hadamard32_amd import linear
     L = layer
 
@@ -234,6 +235,11 @@ def linear_layer(layer, torch, reps: int = 3):
             ("mx_linear_fwd_bwd_ms", linear.MXLinearConfig(fprop_q=spec(L.fprop_q),
                                                             dgrad_q=spec(L.dgrad_q),
                                                             wgrad_q=spec(L.wgrad_q))),
+            ("mx_linear_tiles32_fwd_bwd_ms",  # W and dY in 32x32 tiles, X 1x32, ceil, RNE
+             linear.MXLinearConfig(fprop_q=linear.QuantSpec(scale_rule=1),
+                                   dgrad_q=linear.QuantSpec(scale_rule=1),
+                                   wgrad_q=linear.QuantSpec(scale_rule=1), w_block=32,
+                                   dy_block=32)),
             ("bf16_linear_fwd_bwd_ms", linear.MXLinearConfig(fprop=False, dgrad=False,
                                                               wgrad=False))):
         def run():

@@ -1,4 +1,4 @@
-"""Linear layer whose GEMMs run in MXFP4, one toggle per GEMM.
+"""Linear layer whose GEMMs run in MXFP4 (or MXFP8), one toggle per GEMM.
 
 "Pretraining large language models with MXFP4" (abstract) enables FP4 progressively in the
 forward product (Fprop), the activation gradient (Dgrad) and the weight gradient (Wgrad) of
@@ -12,6 +12,12 @@ product, the comparison arm of that progressive enabling.
     Fprop  Y  [T][N] = X [T][K] W [N][K]^T     X, W along K
     Dgrad  dX [T][K] = dY[T][N] W [N][K]       dY along N, W along N (K-major copy of W^T)
     Wgrad  dW [N][K] = dY^T X                  dY and X along T (K-major copies of dY^T, X^T)
+
+Two variants from the same page:
+  * w_block / dy_block = 32 or 64 ("The fix, and its supporting cast"): W and / or dY are
+    quantized once in square tiles, so the transposed product reads the same codes and scales
+    (the tile's transposed copy) instead of a re-blocked quantization; X stays 1x32.
+  * fmt = "mxfp8": the query / key projections in MXFP8, X and W in E4M3 and dY in E5M2.
 """
 from __future__ import annotations
 
@@ -19,8 +25,9 @@ from dataclasses import dataclass, field
 
 import torch
 
-from . import (MX_ROUND_RNE, MX_SCALE_FLOOR, mx_gemm_dgrad, mx_gemm_fprop, mx_gemm_wgrad,
-               mx_quantize)
+from . import (MX_E4M3, MX_E5M2, MX_ROUND_RNE, MX_SCALE_FLOOR, mx_gemm_dgrad, mx_gemm_fprop,
+               mx_gemm_mxfp8, mx_gemm_wgrad, mx_quantize, mx_quantize_2d_blocks,
+               mx_quantize_mxfp8)
 
 
 @dataclass
@@ -34,12 +41,15 @@ class QuantSpec:
 
 @dataclass
 class MXLinearConfig:
-    fprop: bool = True          # Fprop in MXFP4
-    dgrad: bool = True          # Dgrad in MXFP4
-    wgrad: bool = True          # Wgrad in MXFP4
+    fprop: bool = True          # Fprop in MX format
+    dgrad: bool = True          # Dgrad in MX format
+    wgrad: bool = True          # Wgrad in MX format
     fprop_q: QuantSpec = field(default_factory=QuantSpec)
     dgrad_q: QuantSpec = field(default_factory=QuantSpec)
     wgrad_q: QuantSpec = field(default_factory=QuantSpec)
+    fmt: str = "mxfp4"          # "mxfp4" or "mxfp8"
+    w_block: int = 1            # 1 (1x32 along each GEMM's reduction axis), 32 or 64 (tiles)
+    dy_block: int = 1           # the same for dY
     seed: int = 1234            # Philox key base of stochastic rounding; advanced every call
 
     def next_seeds(self) -> tuple[int, int, int]:
@@ -48,10 +58,32 @@ class MXLinearConfig:
         self.seed += 3
         return s, s + 1, s + 2
 
+    def check(self):
+        if self.fmt not in ("mxfp4", "mxfp8"):
+            raise ValueError("fmt must be 'mxfp4' or 'mxfp8'")
+        if self.w_block not in (1, 32, 64) or self.dy_block not in (1, 32, 64):
+            raise ValueError("w_block and dy_block must be 1, 32 or 64")
+        if self.fmt == "mxfp8" and (self.w_block != 1 or self.dy_block != 1):
+            raise ValueError("MXFP8 operands are 1x32 blocks")
+        tiled = [q for q, on in ((self.fprop_q, self.w_block > 1), (self.dgrad_q, self.w_block > 1
+                 or self.dy_block > 1), (self.wgrad_q, self.dy_block > 1)) if on]
+        if any(q.hadamard for q in tiled):
+            raise ValueError("tiles are quantized without the Hadamard rotation")
 
-def _q(t: torch.Tensor, axis: int, spec: QuantSpec, seed: int):
+
+def _q(t: torch.Tensor, axis: int, spec: QuantSpec, seed: int, fp8: int | None = None):
+    if fp8 is not None:
+        return mx_quantize_mxfp8(t, fmt=fp8, axis=axis, scale_rule=spec.scale_rule,
+                                 round=spec.round, hadamard=spec.hadamard,
+                                 sign_mask=spec.sign_mask, seed=seed)
     return mx_quantize(t, axis=axis, scale_rule=spec.scale_rule, round=spec.round,
                        hadamard=spec.hadamard, sign_mask=spec.sign_mask, seed=seed)
+
+
+def _tiles(t: torch.Tensor, block: int, spec: QuantSpec, seed: int):
+    """(codes, scales, codes_t, scales_t) of block x block tiles; scale granularity = block."""
+    return mx_quantize_2d_blocks(t, block=block, scale_rule=spec.scale_rule, round=spec.round,
+                                 seed=seed)
 
 
 def _alpha(spec: QuantSpec) -> int:
@@ -62,15 +94,28 @@ def _alpha(spec: QuantSpec) -> int:
 class MXLinearFunction(torch.autograd.Function):
     @staticmethod
     def forward(ctx, x: torch.Tensor, w: torch.Tensor, cfg: MXLinearConfig):
+        cfg.check()
         sx, sw, sdy = cfg.next_seeds()
         ctx.cfg, ctx.seeds = cfg, (sx, sw, sdy)
         ctx.save_for_backward(x, w)
-        if cfg.fprop:
-            xq, xs = _q(x, 1, cfg.fprop_q, sx)
-            wq, ws = _q(w, 1, cfg.fprop_q, sw)
-            return mx_gemm_fprop(xq, xs, 1, wq, ws, 1, alpha_exp=_alpha(cfg.fprop_q),
+        ctx.w_tiles = None
+        if not cfg.fprop:
+            if cfg.dgrad and cfg.w_block > 1:
+                ctx.w_tiles = _tiles(w, cfg.w_block, cfg.fprop_q, sw)
+            return x @ w.t()
+        spec = cfg.fprop_q
+        if cfg.fmt == "mxfp8":
+            xq, xs = _q(x, 1, spec, sx, MX_E4M3)
+            wq, ws = _q(w, 1, spec, sw, MX_E4M3)
+            return mx_gemm_mxfp8(xq, xs, MX_E4M3, wq, ws, MX_E4M3, alpha_exp=_alpha(spec),
                                  out_dtype=x.dtype)
-        return x @ w.t()
+        xq, xs = _q(x, 1, spec, sx)
+        if cfg.w_block > 1:
+            ctx.w_tiles = _tiles(w, cfg.w_block, spec, sw)
+            wq, ws, gw = ctx.w_tiles[0], ctx.w_tiles[1], cfg.w_block
+        else:
+            (wq, ws), gw = _q(w, 1, spec, sw), 1
+        return mx_gemm_fprop(xq, xs, 1, wq, ws, gw, alpha_exp=_alpha(spec), out_dtype=x.dtype)
 
     @staticmethod
     def backward(ctx, dy: torch.Tensor):
@@ -78,29 +123,58 @@ class MXLinearFunction(torch.autograd.Function):
         cfg = ctx.cfg
         sx, sw, sdy = ctx.seeds
         dy = dy.contiguous().to(x.dtype)
+        fp8 = cfg.fmt == "mxfp8"
         dx = dw = None
+        dy_tiles = None
+        if cfg.dy_block > 1 and not fp8 and (cfg.dgrad or cfg.wgrad):
+            dy_tiles = _tiles(dy, cfg.dy_block, cfg.dgrad_q if cfg.dgrad else cfg.wgrad_q, sdy)
         if ctx.needs_input_grad[0]:
             if cfg.dgrad:
-                dyq, dys = _q(dy, 1, cfg.dgrad_q, sdy)
-                wtq, wts = _q(w, 0, cfg.dgrad_q, sw)
-                dx = mx_gemm_dgrad(dyq, dys, 1, wtq, wts, 1, alpha_exp=_alpha(cfg.dgrad_q),
-                                   out_dtype=x.dtype)
+                spec = cfg.dgrad_q
+                if fp8:
+                    dyq, dys = _q(dy, 1, spec, sdy, MX_E5M2)
+                    wtq, wts = _q(w, 0, spec, sw, MX_E4M3)
+                    dx = mx_gemm_mxfp8(dyq, dys, MX_E5M2, wtq, wts, MX_E4M3,
+                                       alpha_exp=_alpha(spec), out_dtype=x.dtype)
+                else:
+                    if dy_tiles is not None:
+                        dyq, dys, gdy = dy_tiles[0], dy_tiles[1], cfg.dy_block
+                    else:
+                        (dyq, dys), gdy = _q(dy, 1, spec, sdy), 1
+                    if ctx.w_tiles is not None:
+                        wtq, wts, gwt = ctx.w_tiles[2], ctx.w_tiles[3], cfg.w_block
+                    else:
+                        (wtq, wts), gwt = _q(w, 0, spec, sw), 1
+                    dx = mx_gemm_dgrad(dyq, dys, gdy, wtq, wts, gwt, alpha_exp=_alpha(spec),
+                                       out_dtype=x.dtype)
             else:
                 dx = dy @ w
         if ctx.needs_input_grad[1]:
             if cfg.wgrad:
-                dytq, dyts = _q(dy, 0, cfg.wgrad_q, sdy)
-                xtq, xts = _q(x, 0, cfg.wgrad_q, sx)
-                dw = mx_gemm_wgrad(dytq, dyts, 1, xtq, xts, 1, alpha_exp=_alpha(cfg.wgrad_q),
-                                   out_dtype=w.dtype)
+                spec = cfg.wgrad_q
+                if fp8:
+                    dytq, dyts = _q(dy, 0, spec, sdy, MX_E5M2)
+                    xtq, xts = _q(x, 0, spec, sx, MX_E4M3)
+                    dw = mx_gemm_mxfp8(dytq, dyts, MX_E5M2, xtq, xts, MX_E4M3,
+                                       alpha_exp=_alpha(spec), out_dtype=w.dtype)
+                else:
+                    if dy_tiles is not None:
+                        dytq, dyts, gdy = dy_tiles[2], dy_tiles[3], cfg.dy_block
+                    else:
+                        (dytq, dyts), gdy = _q(dy, 0, spec, sdy), 1
+                    xtq, xts = _q(x, 0, spec, sx)
+                    dw = mx_gemm_wgrad(dytq, dyts, gdy, xtq, xts, 1, alpha_exp=_alpha(spec),
+                                       out_dtype=w.dtype)
             else:
                 dw = dy.t() @ x
+        ctx.w_tiles = None
         return dx, dw, None
 
 
 class MXLinear(torch.nn.Module):
-    """y = x W^T with the products in MXFP4 per MXLinearConfig (no bias). x: [T][K] bf16 with T
-    and K multiples of 32; W: [N][K] bf16 with N a multiple of 32."""
+    """y = x W^T with the products in MX formats per MXLinearConfig (no bias). x: [T][K] bf16 with
+    T and K multiples of 32 (of 128 for MXFP8, of the tile edge for tiled operands); W: [N][K]
+    bf16 with N a multiple of 32 (128, tile edge)."""
 
     def __init__(self, in_features: int, out_features: int, cfg: MXLinearConfig | None = None,
                  device="cuda", dtype=torch.bfloat16):
