@@ -29,7 +29,7 @@ using namespace mxd;
 
 constexpr int kThreads = 256;
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-constexpr int kRowChunksPerThread = 2;
+constexpr int kRowChunksPerThread = 4;
 
 template <bool BF16>
 __device__ __forceinline__ void load8(const void* __restrict__ x, int64_t off, float (&v)[8]) {
