@@ -434,8 +434,8 @@ def main():
         write_traffic(*args.write_traffic, args.workload)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the path's multi-GPU sharding is described in DESIGN.md, not built)",
+        print(f"bench.py: the path runs on one GPU; --gpus {args.gpus} is not supported "
+              "(sharding along tokens with a Wgrad all-reduce is a design, not built)",
               file=sys.stderr)
         sys.exit(2)
     import torch
