@@ -203,3 +203,14 @@ def test_gemm_64_row_granularity_needs_whole_tiles(L):
     assert g(FAKE, FAKE, 64, FAKE, FAKE, 1, 96, 64, 64, 0, 1, FAKE, 64, None) == m.MX_ERR_SHAPE
     assert g(FAKE, FAKE, 1, FAKE, FAKE, 64, 64, 96, 64, 0, 1, FAKE, 96, None) == m.MX_ERR_SHAPE
     assert g(FAKE, FAKE, 16, FAKE, FAKE, 1, 64, 64, 64, 0, 1, FAKE, 64, None) == m.MX_ERR_ARG
+
+
+def test_gemm_rejects_operand_tiles_beyond_32_bit_offsets(L):
+    """A 256-row operand tile must stay below 2 GiB (the kernels' 32-bit buffer offsets): K = 2^24
+    is refused before anything is launched."""
+    from mxfp4_block_scaled_hadamard32_amd import _lib as m
+    K = 1 << 24
+    assert L.mx_gemm_fprop(FAKE, FAKE, 1, FAKE, FAKE, 1, 256, 256, K, 0, 1, FAKE, 256,
+                           None) == m.MX_ERR_LAUNCH
+    assert L.mx_gemm_mxfp8(FAKE, FAKE, 0, FAKE, FAKE, 0, 256, 256, K // 2, 0, 1, FAKE, 256,
+                           None) == m.MX_ERR_LAUNCH
