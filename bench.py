@@ -174,8 +174,9 @@ def cpu_baseline(layer, rows: int):
             "_numpy": np.__version__}
 
 
-def load_traffic(launch_flops_key: str):
-    if not os.path.exists(TRAFFIC_FILE):
+def load_traffic(launch_flops_key: str, workload: str):
+    # the record holds the counters of the llama70b_down launches only
+    if workload != "llama70b_down" or not os.path.exists(TRAFFIC_FILE):
         return None
     rec = json.load(open(TRAFFIC_FILE))
     if rec.get("gemm_sha") != sha(GEMM_SRC):
@@ -308,6 +309,32 @@ def mxfp8_attention(mx, wl, torch, reps: int = 5):
             res[f"mxfp8_{name}_tflops"] = round(tf, 1)
             res[f"mxfp8_{name}_pct_of_fp8_peak"] = round(100.0 * tf / PEAK_FP8_TFLOPS, 2)
     return res
+
+
+def quant_stream(mx, wl, torch, reps: int = 20):
+    """Outside the timed step: the quantize-only stream workload exactly (A 8192x4096 bf16 ~ t(3)
+    with 0.5% of channels x100; random-sign Hadamard32, ceil scale, SR with Philox key 1234),
+    along rows, at 2.53125 algorithmic B/element."""
+    A = wl.quant_stream(device="cuda")["A"]
+    rows, cols = A.shape
+    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device="cuda")
+
+    def run():
+        mx.mx_quantize(A, scale_rule=1, round=1, hadamard=1, sign_mask=wl.sign_mask(),
+                       seed=wl.SR_SEED, codes=codes, scales=scales)
+    run()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    gbs = rows * cols * QUANT_BYTES_PER_ELEM / (ms * 1e-3) / 1e9
+    return {"quant_stream_8192x4096_ms": round(ms, 4), "quant_stream_8192x4096_gbs": round(gbs, 1),
+            "quant_stream_8192x4096_pct_of_hbm_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2)}
 
 
 def block_variants(mx, wl, torch, reps: int = 5):
@@ -476,7 +503,7 @@ def main():
     wgrad_tflops = layer.flops["wgrad"] / (wgrad_ms * 1e-3) / 1e12
     qelems = layer.T * layer.K
     quant_gbs = qelems * QUANT_BYTES_PER_ELEM / (quant_ms * 1e-3) / 1e9
-    traffic = load_traffic("wgrad_hbm_bytes_per_launch")
+    traffic = load_traffic("wgrad_hbm_bytes_per_launch", args.workload)
 
     out = {
         "metric": METRIC,
@@ -516,6 +543,7 @@ def main():
         out["components"].update(fused_epilogue(layer, torch))
         out["components"].update(linear_layer(layer, torch))
     if not args.step_only or args.with_variants:
+        out["components"].update(quant_stream(mx, wl, torch))
         out["components"].update(mxfp8_attention(mx, wl, torch))
         out["components"].update(block_variants(mx, wl, torch))
     if not args.no_cpu_baseline:
