@@ -260,9 +260,11 @@ __global__ __launch_bounds__(kThreads) void quant_2d_kernel(
     const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, uint64_t seed,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, uint8_t* __restrict__ codes_t,
     uint8_t* __restrict__ scales_t, int64_t n_ct) {
-  __shared__ __attribute__((aligned(16))) uint8_t rtile[k2dTile * k2dStride];  // [row][col/2]
-  __shared__ __attribute__((aligned(16))) uint8_t ttile[k2dTile * k2dStride];  // [col][row/2]
+  // one code tile, used for the row-major codes and then for the transposed ones (half the LDS
+  // of two tiles, so twice the workgroups per CU); each lane keeps its 4 patches' codes
+  __shared__ __attribute__((aligned(16))) uint8_t ctile[k2dTile * k2dStride];  // [row or col][../2]
   __shared__ uint8_t stile[64];                                                 // [rb][cb]
+  uint32_t Rk[4][8];  // codes of pass p: patch row j (nibble k = column k)
   const int64_t rt = blockIdx.x / n_ct, ct = blockIdx.x - rt * n_ct;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int q = lane & 3, cgl = lane >> 2;  // cgl = 4 * tile + column-group, 0..15
@@ -311,18 +313,17 @@ __global__ __launch_bounds__(kThreads) void quant_2d_kernel(
     }
     const int rl0 = rbl * 32 + 8 * q;  // first row of the patch within the tile
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      *reinterpret_cast<uint32_t*>(rtile + (rl0 + j) * k2dStride + cl0 / 2) = R[j];
-    transpose_nibbles8x8(R);  // R[k] = codes of patch column k (nibble j = row j)
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      *reinterpret_cast<uint32_t*>(ttile + (cl0 + k) * k2dStride + rl0 / 2) = R[k];
+    for (int j = 0; j < 8; ++j) {
+      *reinterpret_cast<uint32_t*>(ctile + (rl0 + j) * k2dStride + cl0 / 2) = R[j];
+      Rk[pass][j] = R[j];
+    }
     if ((lane & 15) == 0) stile[rbl * 8 + cl0 / 32] = (uint8_t)sb;
   }
   __syncthreads();
 
   // codes: 8 lanes per row (column) of the tile, 16 bytes each: every store instruction writes
-  // the whole 128-byte pieces of 8 rows
+  // the whole 128-byte pieces of 8 rows; first the row-major codes, then (the tile refilled
+  // with the transposed patches) the codes of the transpose
   const int64_t cols2 = cols / 2, rows2 = rows / 2;
   const int seg = threadIdx.x & 7;
 #pragma unroll
@@ -330,12 +331,31 @@ __global__ __launch_bounds__(kThreads) void quant_2d_kernel(
     const int i = round * (kThreads / 8) + (threadIdx.x >> 3);
     if (i < nrb * 32 && seg < ncb)  // a 32-column block is one 16-byte segment
       __builtin_nontemporal_store(
-          *reinterpret_cast<const u32x4*>(rtile + i * k2dStride + 16 * seg),
+          *reinterpret_cast<const u32x4*>(ctile + i * k2dStride + 16 * seg),
           reinterpret_cast<u32x4*>(codes + (rtile0 + i) * cols2 + ctile0 / 2 + 16 * seg));
-    if (codes_t && i < ncb * 32 && seg < nrb)
-      __builtin_nontemporal_store(
-          *reinterpret_cast<const u32x4*>(ttile + i * k2dStride + 16 * seg),
-          reinterpret_cast<u32x4*>(codes_t + (ctile0 + i) * rows2 + rtile0 / 2 + 16 * seg));
+  }
+  if (codes_t) {
+    __syncthreads();  // every row-major piece has been read from the tile
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+      const int rbl = (pass & 1) * 4 + wave, ch = pass >> 1;
+      const int cl0 = ch * 128 + cgl * 8;
+      if (rbl >= nrb || cl0 >= ncb * 32) continue;
+      transpose_nibbles8x8(Rk[pass]);  // Rk[pass][k] = codes of patch column k (nibble j = row j)
+      const int rl0 = rbl * 32 + 8 * q;
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        *reinterpret_cast<uint32_t*>(ctile + (cl0 + k) * k2dStride + rl0 / 2) = Rk[pass][k];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int round = 0; round < k2dTile * 8 / kThreads; ++round) {
+      const int i = round * (kThreads / 8) + (threadIdx.x >> 3);
+      if (i < ncb * 32 && seg < nrb)
+        __builtin_nontemporal_store(
+            *reinterpret_cast<const u32x4*>(ctile + i * k2dStride + 16 * seg),
+            reinterpret_cast<u32x4*>(codes_t + (ctile0 + i) * rows2 + rtile0 / 2 + 16 * seg));
+    }
   }
   // scales: thread t < 64 writes tile (t / 8, t % 8) to both layouts
   if (threadIdx.x < 64) {
@@ -366,9 +386,10 @@ __global__ __launch_bounds__(kThreads) void quant_2d_var_kernel(
     uint8_t* __restrict__ scales_t, int64_t n_ct) {
   static_assert(B == 8 || B == 64, "8x8 or 64x64 tiles");
   constexpr int NS = k2dTile / B;  // tiles per edge of the workgroup tile
-  __shared__ __attribute__((aligned(16))) uint8_t rtile[k2dTile * k2dStride];  // [row][col/2]
-  __shared__ __attribute__((aligned(16))) uint8_t ttile[k2dTile * k2dStride];  // [col][row/2]
+  // one code tile for the row-major codes, then the transposed ones (as in the 32x32 kernel)
+  __shared__ __attribute__((aligned(16))) uint8_t ctile[k2dTile * k2dStride];  // [row or col][../2]
   __shared__ __attribute__((aligned(16))) uint8_t stile[NS * NS];               // [tr][tc]
+  uint32_t Rk[4][8];  // codes of pass p: patch row j (nibble k = column k)
   const int64_t rt = blockIdx.x / n_ct, ct = blockIdx.x - rt * n_ct;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int pr = lane >> 3, pc = lane & 7;
@@ -424,18 +445,17 @@ __global__ __launch_bounds__(kThreads) void quant_2d_var_kernel(
       }
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      *reinterpret_cast<uint32_t*>(rtile + (rl0 + j) * k2dStride + cl0 / 2) = R[j];
-    transpose_nibbles8x8(R);  // R[k] = codes of patch column k (nibble j = row j)
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      *reinterpret_cast<uint32_t*>(ttile + (cl0 + k) * k2dStride + rl0 / 2) = R[k];
+    for (int j = 0; j < 8; ++j) {
+      *reinterpret_cast<uint32_t*>(ctile + (rl0 + j) * k2dStride + cl0 / 2) = R[j];
+      Rk[pass][j] = R[j];
+    }
     if (B == 8) stile[(rl0 / 8) * NS + cl0 / 8] = (uint8_t)sb;
     else if (lane == 0) stile[sr * NS + sc] = (uint8_t)sb;
   }
   __syncthreads();
 
-  // codes: 8 lanes per row (column) of the tile, 16 bytes (32 codes) each
+  // codes: 8 lanes per row (column) of the tile, 16 bytes (32 codes) each; the row-major codes
+  // first, then the tile refilled with the transposed patches
   const int64_t cols2 = cols / 2, rows2 = rows / 2;
   const int seg = threadIdx.x & 7;
 #pragma unroll
@@ -443,12 +463,34 @@ __global__ __launch_bounds__(kThreads) void quant_2d_var_kernel(
     const int i = round * (kThreads / 8) + (threadIdx.x >> 3);
     if (i < nr && 32 * seg < nc)
       __builtin_nontemporal_store(
-          *reinterpret_cast<const u32x4*>(rtile + i * k2dStride + 16 * seg),
+          *reinterpret_cast<const u32x4*>(ctile + i * k2dStride + 16 * seg),
           reinterpret_cast<u32x4*>(codes + (rtile0 + i) * cols2 + ctile0 / 2 + 16 * seg));
-    if (codes_t && i < nc && 32 * seg < nr)
-      __builtin_nontemporal_store(
-          *reinterpret_cast<const u32x4*>(ttile + i * k2dStride + 16 * seg),
-          reinterpret_cast<u32x4*>(codes_t + (ctile0 + i) * rows2 + rtile0 / 2 + 16 * seg));
+  }
+  if (codes_t) {
+    __syncthreads();  // every row-major piece has been read from the tile
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+      const int t = 4 * pass + wave, sr = t >> 2, sc = t & 3;
+      const int rl0 = 64 * sr + 8 * pr, cl0 = 64 * sc + 8 * pc;
+      if (B == 64) {
+        if (64 * sr >= nr || 64 * sc >= nc) continue;
+      } else if (rl0 >= nr || cl0 >= nc) {
+        continue;
+      }
+      transpose_nibbles8x8(Rk[pass]);  // Rk[pass][k] = codes of patch column k (nibble j = row j)
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        *reinterpret_cast<uint32_t*>(ctile + (cl0 + k) * k2dStride + rl0 / 2) = Rk[pass][k];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int round = 0; round < k2dTile * 8 / kThreads; ++round) {
+      const int i = round * (kThreads / 8) + (threadIdx.x >> 3);
+      if (i < nc && 32 * seg < nr)
+        __builtin_nontemporal_store(
+            *reinterpret_cast<const u32x4*>(ctile + i * k2dStride + 16 * seg),
+            reinterpret_cast<u32x4*>(codes_t + (ctile0 + i) * rows2 + rtile0 / 2 + 16 * seg));
+    }
   }
   if (B == 8) {
     // thread t: scale row (column) t / 8 of the tile, 4 bytes (32 source columns) at t % 8
