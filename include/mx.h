@@ -101,8 +101,9 @@ typedef struct {
  * sign_mask and apply the unnormalised 32-point Sylvester-Hadamard transform
  * H[i][j] = (-1)^popcount(i & j) as five fp32 butterfly stages of span 1, 2, 4, 8, 16;
  * block maximum; scale exponent; v = x * 2^-e in fp32; round; pack.
- * Alignment: x and every source row (ld * element size) 16 bytes; codes 4 bytes (axis = 1) or
- * 16 bytes (axis = 0); axis = 0 also needs cols % 8 == 0.
+ * Alignment: x and every source row (ld * element size) 16 bytes; codes 16 bytes (a code row
+ * is a multiple of 16 bytes, so any row slice of an aligned buffer qualifies); axis = 0 also
+ * needs cols % 8 == 0.
  * Errors (nothing is launched): MX_ERR_NULL for a NULL x, codes, scales or opts;
  * MX_ERR_SHAPE for negative sizes, ld < cols or a multiple-of-32 / row-alignment rule;
  * MX_ERR_ARG for a bad dtype, axis or option value, or a misaligned pointer;

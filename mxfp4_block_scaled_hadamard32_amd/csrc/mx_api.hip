@@ -68,8 +68,8 @@ mx_status mx_quantize(const void* x, int32_t dtype, int64_t rows, int64_t cols, 
   if (axis == 0 && (rows % 32 != 0 || cols % 8 != 0)) return MX_ERR_SHAPE;
   if (rows == 0 || cols == 0) return MX_OK;
   if (!x || !codes || !scales) return MX_ERR_NULL;
-  // rows: one dword of codes per lane; columns: 16-byte pieces of transposed code rows
-  if (!aligned(codes, axis == 1 ? 4 : 16)) return MX_ERR_ARG;
+  // rows: the 16 code bytes of a block per lane; columns: 16-byte pieces of transposed code rows
+  if (!aligned(codes, 16)) return MX_ERR_ARG;
   QuantArgs a{x, dtype == MX_BF16, rows, cols, ld, axis, opts->scale_rule == MX_SCALE_CEIL,
               opts->round == MX_ROUND_SR, opts->hadamard == 1, opts->sign_mask, opts->seed,
               codes, scales, nullptr, nullptr, stream};

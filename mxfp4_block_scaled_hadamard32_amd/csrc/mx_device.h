@@ -127,21 +127,52 @@ __device__ __forceinline__ uint32_t cvt_rne_pack8(const float (&v)[8]) {
   return w;
 }
 
-// The converter writes the pair's codes to byte 0 (the first value in the low nibble); the
-// pair's second value is a zero whose code is discarded, and the nibble is
-// placed by hand (the compiler does not carry the untouched bytes of the destination through
-// this builtin, so byte selection cannot accumulate a word). rw[k] = (~r_k << 16) | 0xFFFF.
+// One stochastic conversion into byte BYTE of acc: the converter writes the codes of its pair
+// (value, 0) to that byte, the value's code in the low nibble and the zero's code (0) in the high
+// one, and keeps the other three bytes. The compiler's builtin for this instruction does not
+// model the kept bytes, so the instruction is written out with acc tied to its destination
+// (byte 0 starts a word: whatever the other bytes held is overwritten by the later bytes). A
+// VALU read of a register written with a byte select needs one wait state on gfx950, hence the
+// s_nop. rw = (~r << 16) | 0xFFFF; the input is the value rounded up to a multiple of 2^-23,
+// times 2^23, so the scale operand is 2^23.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+template <int BYTE>
+__device__ __forceinline__ void cvt_sr_fp4_byte(uint32_t& acc, float up, uint32_t rw) {
+  const f32x2_t pair = {up, 0.0f};
+  const float scale = 8388608.0f;
+  if constexpr (BYTE == 0)
+    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3\n\ts_nop 0"
+        : "=v"(acc) : "v"(pair), "v"(rw), "s"(scale));
+  else if constexpr (BYTE == 1)
+    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3 op_sel:[0,0,1,0]\n\ts_nop 0"
+        : "+v"(acc) : "v"(pair), "v"(rw), "s"(scale));
+  else if constexpr (BYTE == 2)
+    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3 op_sel:[0,0,0,1]\n\ts_nop 0"
+        : "+v"(acc) : "v"(pair), "v"(rw), "s"(scale));
+  else
+    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3 op_sel:[0,0,1,1]\n\ts_nop 0"
+        : "+v"(acc) : "v"(pair), "v"(rw), "s"(scale));
+}
+
+// |v| rounded up to a multiple of 2^-23, times 2^23, with the sign of v
+__device__ __forceinline__ float sr_round_up23(float v) {
+  return __builtin_copysignf(__builtin_ceilf(fabsf(v) * 8388608.0f), v);
+}
+
+// 8 scaled values -> 8 codes (value k in nibble k). Even values go to bytes 0-3 of one word and
+// odd values to bytes 0-3 of another, each code in the low nibble of its byte; the odd word is
+// then shifted into the high nibbles. rw[k] = (~r_k << 16) | 0xFFFF.
 __device__ __forceinline__ uint32_t sr_pack8(const float (&v)[8], const uint32_t (&rw)[8]) {
-  typedef float f32x2_t __attribute__((ext_vector_type(2)));
-  uint32_t w = 0;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const float up = __builtin_ceilf(fabsf(v[k]) * 8388608.0f);  // |v| up to 2^-23, times 2^23
-    const f32x2_t pair = {__builtin_copysignf(up, v[k]), 0.0f};
-    const uint32_t code = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, pair, rw[k], 8388608.0f, 0);
-    w |= (code & 0xFu) << (4 * k);
-  }
-  return w;
+  uint32_t ev, od;
+  cvt_sr_fp4_byte<0>(ev, sr_round_up23(v[0]), rw[0]);
+  cvt_sr_fp4_byte<0>(od, sr_round_up23(v[1]), rw[1]);
+  cvt_sr_fp4_byte<1>(ev, sr_round_up23(v[2]), rw[2]);
+  cvt_sr_fp4_byte<1>(od, sr_round_up23(v[3]), rw[3]);
+  cvt_sr_fp4_byte<2>(ev, sr_round_up23(v[4]), rw[4]);
+  cvt_sr_fp4_byte<2>(od, sr_round_up23(v[5]), rw[5]);
+  cvt_sr_fp4_byte<3>(ev, sr_round_up23(v[6]), rw[6]);
+  cvt_sr_fp4_byte<3>(od, sr_round_up23(v[7]), rw[7]);
+  return ev | (od << 4);
 }
 
 // ---------------------------------------------------------------------------------------------

@@ -47,38 +47,114 @@ __device__ __forceinline__ void load8(const void* __restrict__ x, int64_t off, f
 }
 
 // ---------------------------------------------------------------------------------------------
-// 1x32 blocks along rows. Chunk g = 8 consecutive elements, row-major over the logical tensor,
-// so element index 8g + k is also the stochastic-rounding index.
+// 1x32 blocks along rows: one lane per block. Block b = row * (cols / 32) + column block is
+// source elements 32 b .. 32 b + 31 of the logical tensor, so its 8-element groups have the
+// stochastic-rounding chunk indices 4 b .. 4 b + 3. With the whole block in one lane, every
+// butterfly stage, the maximum and the scale stay in registers (no lane exchanges, one scale
+// computation per block); a wave reads 64 whole blocks and writes 1 KiB of codes and 64 scale
+// bytes, each a contiguous piece.
 // ---------------------------------------------------------------------------------------------
+// Widen 8 bf16 values (one 16-byte load) and apply the random signs of block positions
+// p0 .. p0+7: the sign of position j is bit j of sign_mask (the same for every lane). Adding
+// 2^31 toggles bit 31 exactly as a XOR does, so the low value takes one shift-add and the high
+// value one and-xor.
+template <bool HAD>
+__device__ __forceinline__ void widen_signed8(const u32x4 raw, uint32_t sign_mask, int p0,
+                                              float* v) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t s0 = HAD ? ((sign_mask >> (p0 + 2 * i)) & 1u) << 31 : 0u;
+    const uint32_t s1 = HAD ? ((sign_mask >> (p0 + 2 * i + 1)) & 1u) << 31 : 0u;
+    v[2 * i] = __uint_as_float((w[i] << 16) + s0);
+    v[2 * i + 1] = __uint_as_float((w[i] & 0xFFFF0000u) ^ s1);
+  }
+}
+
 template <bool BF16, bool HAD, bool SR, bool CEIL>
 __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
-    const void* __restrict__ x, int64_t nchunks, int64_t cpr, int64_t ld, int contiguous,
-    uint32_t sign_mask, uint64_t seed, uint32_t* __restrict__ codes, uint8_t* __restrict__ scales) {
-  const int q = threadIdx.x & 3;
-
-  const int64_t base = (int64_t)blockIdx.x * (kThreads * kRowChunksPerThread) + threadIdx.x;
-  float v[kRowChunksPerThread][8];
+    const void* __restrict__ x, int64_t nblk, int64_t bpr, int64_t ld, int contiguous,
+    uint32_t sign_mask, uint64_t seed, u32x4* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (b >= nblk) return;
+  int64_t off = 32 * b;
+  if (!contiguous) {
+    const int64_t r = b / bpr;
+    off = r * ld + 32 * (b - r * bpr);
+  }
+  float w[32];
+  if (BF16) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(x) + off);
+    u32x4 raw[4];
 #pragma unroll
-  for (int u = 0; u < kRowChunksPerThread; ++u) {
-    const int64_t g = base + (int64_t)u * kThreads;
-    if (g < nchunks) {
-      int64_t off = 8 * g;
-      if (!contiguous) {
-        const int64_t r = g / cpr;
-        off = r * ld + 8 * (g - r * cpr);
-      }
-      load8<BF16>(x, off, v[u]);
+    for (int i = 0; i < 4; ++i) raw[i] = __builtin_nontemporal_load(p + i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) widen_signed8<HAD>(raw[i], sign_mask, 8 * i, w + 8 * i);
+  } else {
+    const f32x4* p = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(x) + off);
+    f32x4 raw[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) raw[i] = __builtin_nontemporal_load(p + i);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      w[4 * i] = raw[i].x; w[4 * i + 1] = raw[i].y; w[4 * i + 2] = raw[i].z; w[4 * i + 3] = raw[i].w;
+    }
+    if (HAD) {
+#pragma unroll
+      for (int j = 0; j < 32; ++j)
+        w[j] = __uint_as_float(__float_as_uint(w[j]) ^ (((sign_mask >> j) & 1u) << 31));
     }
   }
+  // 32-point transform [P1 paragraph 2]: spans 1, 2, 4, 8, 16, each output one IEEE add or
+  // subtract of the stage's two inputs
+  if (HAD) {
 #pragma unroll
-  for (int u = 0; u < kRowChunksPerThread; ++u) {
-    const int64_t g = base + (int64_t)u * kThreads;
-    if (g >= nchunks) continue;  // quads are all in or all out (cols % 32 == 0)
-    uint32_t sb;
-    const uint32_t word = quant_chunk8<HAD, SR, CEIL>(v[u], q, sign_mask, seed, (uint64_t)g, sb);
-    __builtin_nontemporal_store(word, codes + g);
-    if (q == 0) scales[g >> 2] = (uint8_t)sb;
+    for (int h = 1; h < 32; h <<= 1) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        if (i & h) continue;
+        const float a = w[i], c = w[i + h];
+        w[i] = a + c;
+        w[i + h] = a - c;
+      }
+    }
   }
+  // block maximum of |x| as bits: the unsigned maximum of the raw bits is the largest negative
+  // value (if any), the signed maximum the largest positive one (if any); with the sign bits
+  // cleared the larger of the two is the largest magnitude, NaN and infinity included
+  uint32_t mu = __float_as_uint(w[0]);
+  int32_t mi = (int32_t)mu;
+#pragma unroll
+  for (int j = 1; j < 31; j += 2) {  // one three-input maximum per two values
+    mu = max(max(mu, __float_as_uint(w[j])), __float_as_uint(w[j + 1]));
+    mi = max(max(mi, (int32_t)__float_as_uint(w[j])), (int32_t)__float_as_uint(w[j + 1]));
+  }
+  mu = max(mu, __float_as_uint(w[31]));
+  mi = max(mi, (int32_t)__float_as_uint(w[31]));
+  const uint32_t m = max(mu & 0x7FFFFFFFu, (uint32_t)mi & 0x7FFFFFFFu);
+  const uint32_t sb = scale_byte<CEIL>(m);
+  u32x4 out = {0u, 0u, 0u, 0u};
+  if (sb != 0xFFu) {
+    const float inv = inv_scale_from_byte(sb);
+#pragma unroll
+    for (int j = 0; j < 32; ++j) w[j] = w[j] * inv;
+    uint32_t o[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      float* c = w + 8 * d;
+      const float (&v8)[8] = *reinterpret_cast<const float(*)[8]>(c);
+      if (SR) {
+        uint32_t rw[8];
+        sr_rand8((uint64_t)(4 * b + d), seed, rw);
+        o[d] = sr_pack8(v8, rw);
+      } else {
+        o[d] = cvt_rne_pack8(v8);
+      }
+    }
+    out = u32x4{o[0], o[1], o[2], o[3]};
+  }
+  __builtin_nontemporal_store(out, codes + b);
+  scales[b] = (uint8_t)sb;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -745,14 +821,13 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(
 // ---------------------------------------------------------------------------------------------
 template <bool BF16, bool HAD, bool SR, bool CEIL>
 hipError_t launch_rows(const QuantArgs& a) {
-  const int64_t cpr = a.cols / 8;
-  const int64_t nchunks = a.rows * cpr;
-  const int64_t per_block = kThreads * kRowChunksPerThread;
-  const int64_t nblocks = (nchunks + per_block - 1) / per_block;
+  const int64_t bpr = a.cols / 32;
+  const int64_t nblk = a.rows * bpr;
+  const int64_t nblocks = (nblk + kThreads - 1) / kThreads;
   if (nblocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL((quant_rows_kernel<BF16, HAD, SR, CEIL>), dim3((unsigned)nblocks), dim3(kThreads),
-                     0, (hipStream_t)a.stream, a.x, nchunks, cpr, a.ld, a.ld == a.cols ? 1 : 0,
-                     a.sign_mask, a.seed, reinterpret_cast<uint32_t*>(a.codes), a.scales);
+                     0, (hipStream_t)a.stream, a.x, nblk, bpr, a.ld, a.ld == a.cols ? 1 : 0,
+                     a.sign_mask, a.seed, reinterpret_cast<u32x4*>(a.codes), a.scales);
   return hipGetLastError();
 }
 

@@ -64,6 +64,9 @@ def test_quantize_argument_errors(L):
     assert q(None, 1, 64, 64, 64, 1, opts(), FAKE, FAKE, None) == m.MX_ERR_NULL
     assert q(FAKE, 1, 64, 64, 64, 1, opts(), None, FAKE, None) == m.MX_ERR_NULL
     assert q(ctypes.c_void_p(0x10008), 1, 64, 64, 64, 1, opts(), FAKE, FAKE, None) == m.MX_ERR_ARG
+    # codes: 16 bytes for both axes (a lane writes a block's 16 code bytes at once)
+    assert q(FAKE, 1, 64, 64, 64, 1, opts(), ctypes.c_void_p(0x10008), FAKE, None) == m.MX_ERR_ARG
+    assert q(FAKE, 1, 64, 64, 64, 0, opts(), ctypes.c_void_p(0x10004), FAKE, None) == m.MX_ERR_ARG
     # empty tensors are fine and launch nothing
     assert q(None, 1, 0, 64, 64, 1, opts(), None, None, None) == m.MX_OK
     assert q(None, 1, 32, 0, 0, 0, opts(), None, None, None) == m.MX_OK
