@@ -71,33 +71,69 @@ __device__ __forceinline__ void widen_signed8(const u32x4 raw, uint32_t sign_mas
   }
 }
 
+// The 16-byte pieces of a block are loaded with consecutive lanes on consecutive pieces (whole
+// lines per instruction) and regrouped per block through the wave's own LDS area: piece c of
+// block B sits at slot C B + (c ^ ((B >> log2(16 / C)) % C)), C pieces per block, so that both
+// the writes (16 consecutive pieces) and the reads (piece j of 16 consecutive blocks) cover all
+// banks. With a leading dimension other than cols the blocks are loaded directly per lane.
+template <bool BF16>
+__device__ __forceinline__ int row_slot(int blk, int c) {
+  constexpr int C = BF16 ? 4 : 8, SH = BF16 ? 2 : 1;
+  return C * blk + (c ^ ((blk >> SH) & (C - 1)));
+}
+
 template <bool BF16, bool HAD, bool SR, bool CEIL>
 __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
     const void* __restrict__ x, int64_t nblk, int64_t bpr, int64_t ld, int contiguous,
     uint32_t sign_mask, uint64_t seed, u32x4* __restrict__ codes, uint8_t* __restrict__ scales) {
-  const int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (b >= nblk) return;
-  int64_t off = 32 * b;
-  if (!contiguous) {
+  constexpr int C = BF16 ? 4 : 8;  // 16-byte pieces per block
+  __shared__ __attribute__((aligned(16))) u32x4 stage[kThreads * C];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t wb = (int64_t)blockIdx.x * kThreads + wave * 64;  // the wave's first block
+  const int64_t b = wb + lane;
+  u32x4 raw[C];
+  if (wb >= nblk) return;  // uniform per wave
+  if (contiguous) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(
+        reinterpret_cast<const uint8_t*>(x) + wb * 32 * (BF16 ? 2 : 4));
+    u32x4* st = stage + wave * 64 * C;
+    // all loads first (pieces of blocks past the end re-read the wave's first piece; their
+    // slots are never read back), then the LDS writes
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+      const int pc = 64 * i + lane;  // piece of the wave's range
+      raw[i] = __builtin_nontemporal_load(src + (wb + pc / C < nblk ? pc : 0));
+    }
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+      const int pc = 64 * i + lane;
+      st[row_slot<BF16>(pc / C, pc % C)] = raw[i];
+    }
+    // only this wave reads its area: a wave-scope release/acquire orders the accesses (the
+    // lanes of a wave run in lockstep and the wave's LDS operations complete in order)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int i = 0; i < C; ++i) raw[i] = st[row_slot<BF16>(lane, i)];
+    if (b >= nblk) return;
+  } else {
+    if (b >= nblk) return;
     const int64_t r = b / bpr;
-    off = r * ld + 32 * (b - r * bpr);
+    const u32x4* src = reinterpret_cast<const u32x4*>(
+        reinterpret_cast<const uint8_t*>(x) + (r * ld + 32 * (b - r * bpr)) * (BF16 ? 2 : 4));
+#pragma unroll
+    for (int i = 0; i < C; ++i) raw[i] = __builtin_nontemporal_load(src + i);
   }
   float w[32];
   if (BF16) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(x) + off);
-    u32x4 raw[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) raw[i] = __builtin_nontemporal_load(p + i);
 #pragma unroll
     for (int i = 0; i < 4; ++i) widen_signed8<HAD>(raw[i], sign_mask, 8 * i, w + 8 * i);
   } else {
-    const f32x4* p = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(x) + off);
-    f32x4 raw[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) raw[i] = __builtin_nontemporal_load(p + i);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      w[4 * i] = raw[i].x; w[4 * i + 1] = raw[i].y; w[4 * i + 2] = raw[i].z; w[4 * i + 3] = raw[i].w;
+      w[4 * i] = __uint_as_float(raw[i].x); w[4 * i + 1] = __uint_as_float(raw[i].y);
+      w[4 * i + 2] = __uint_as_float(raw[i].z); w[4 * i + 3] = __uint_as_float(raw[i].w);
     }
     if (HAD) {
 #pragma unroll
