@@ -180,21 +180,32 @@ __device__ __forceinline__ uint32_t sr_pack8(const float (&v)[8], const uint32_t
 // counter words 0 and 2 with the Philox multipliers, mixed with words 1, 3 and the key; the key
 // advances by the Weyl constants between rounds. Returns the 128-bit output.
 // ---------------------------------------------------------------------------------------------
+// One round: two 32x32->64 products, their high words mixed with words 1, 3 and the key by a
+// three-input bit operation (TT = 0x96 is a ^ b ^ c, 0x69 its complement).
+template <int TT>
+__device__ __forceinline__ void philox_round(uint32_t& c0, uint32_t& c1, uint32_t& c2,
+                                             uint32_t& c3, uint32_t k0, uint32_t k1) {
+  const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+  const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+  const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, TT);
+  const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, TT);
+  c1 = (uint32_t)p1;
+  c3 = (uint32_t)p0;
+  c0 = n0;
+  c2 = n2;
+}
+
+// INV02: return words 0 and 2 complemented (the last round's XOR becomes an XNOR for free).
+template <bool INV02 = false>
 __device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
                                                uint32_t k0, uint32_t k1) {
 #pragma unroll
-  for (int round = 0; round < 10; ++round) {
-    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
-    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
-    const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, 0x96);  // a^b^c
-    const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x96);
-    c1 = (uint32_t)p1;
-    c3 = (uint32_t)p0;
-    c0 = n0;
-    c2 = n2;
+  for (int round = 0; round < 9; ++round) {
+    philox_round<0x96>(c0, c1, c2, c3, k0, k1);
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
   }
+  philox_round<INV02 ? 0x69 : 0x96>(c0, c1, c2, c3, k0, k1);
   return make_uint4(c0, c1, c2, c3);
 }
 
@@ -202,9 +213,9 @@ __device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
 // field k (16 bits) of the Philox output at counter g (the low half of output word k / 2 for
 // even k, the high half for odd k).
 __device__ __forceinline__ void sr_rand8(uint64_t g, uint64_t seed, uint32_t (&rw)[8]) {
-  const uint4 w = philox4x32_10((uint32_t)g, (uint32_t)(g >> 32), 0u, 0u, (uint32_t)seed,
-                                (uint32_t)(seed >> 32));
-  const uint32_t nw[4] = {~w.x, ~w.y, ~w.z, ~w.w};
+  const uint4 w = philox4x32_10<true>((uint32_t)g, (uint32_t)(g >> 32), 0u, 0u, (uint32_t)seed,
+                                      (uint32_t)(seed >> 32));
+  const uint32_t nw[4] = {w.x, ~w.y, w.z, ~w.w};  // words 0 and 2 come complemented
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     rw[2 * i] = (nw[i] << 16) | 0xFFFFu;

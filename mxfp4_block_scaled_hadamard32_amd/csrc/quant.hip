@@ -204,17 +204,38 @@ __device__ __forceinline__ void load_patch(const void* __restrict__ x, int64_t l
   for (int j = 0; j < 8; ++j) load8<BF16>(x, (r0 + j) * ld + c0, p[j]);
 }
 
-// Column transform of a patch stack: position 8q + j of the 32-block is patch row j of quad
-// lane q. Negate the rows selected by sign_mask, then the five butterfly stages per column.
-__device__ __forceinline__ void fwht_columns(float (&p)[8][8], uint32_t sign_mask, int q) {
-  const uint32_t up8 = (q & 1) ? 0x80000000u : 0u;
-  const uint32_t up16 = (q & 2) ? 0x80000000u : 0u;
+// Patch loader with the random signs of the column transform applied: position 8q + j of the
+// 32-block is patch row j of quad lane q, negated when bit 8q + j of sign_mask is set. For bf16
+// the sign goes in with the widening (adding 2^31 toggles bit 31 as a XOR does).
+template <bool BF16>
+__device__ __forceinline__ void load_patch_signed(const void* __restrict__ x, int64_t ld,
+                                                  int64_t r0, int64_t c0, uint32_t sign_mask,
+                                                  int q, float (&p)[8][8]) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const uint32_t s = ((sign_mask >> (8 * q + j)) & 1u) << 31;
+    if (BF16) {
+      const u32x4 raw = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(x) + (r0 + j) * ld + c0));
+      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-    for (int k = 0; k < 8; ++k) p[j][k] = __uint_as_float(__float_as_uint(p[j][k]) ^ s);
+      for (int i = 0; i < 4; ++i) {
+        p[j][2 * i] = __uint_as_float((w[i] << 16) + s);
+        p[j][2 * i + 1] = __uint_as_float((w[i] & 0xFFFF0000u) ^ s);
+      }
+    } else {
+      load8<false>(x, (r0 + j) * ld + c0, p[j]);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) p[j][k] = __uint_as_float(__float_as_uint(p[j][k]) ^ s);
+    }
   }
+}
+
+// Column transform of a patch stack (signs already applied): the five butterfly stages per
+// column, spans 1, 2, 4 down the lane's patch rows and 8, 16 across the quad.
+__device__ __forceinline__ void fwht_columns(float (&p)[8][8], int q) {
+  const uint32_t up8 = (q & 1) ? 0x80000000u : 0u;
+  const uint32_t up16 = (q & 2) ? 0x80000000u : 0u;
 #pragma unroll
   for (int h = 1; h < 8; h <<= 1) {
 #pragma unroll
@@ -290,8 +311,12 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
     const int64_t rb = rb0 + rbl;
     const int64_t r0 = rb * 32 + 8 * q;
     float p[8][8];
-    load_patch<BF16>(x, ld, r0, c0, p);
-    if (HAD) fwht_columns(p, sign_mask, q);
+    if (HAD) {
+      load_patch_signed<BF16>(x, ld, r0, c0, sign_mask, q, p);
+      fwht_columns(p, q);
+    } else {
+      load_patch<BF16>(x, ld, r0, c0, p);
+    }
 
     uint32_t sb[8];
 #pragma unroll
@@ -744,8 +769,12 @@ __global__ __launch_bounds__(kThreads) void quant_cols_fp8_kernel(
     if (rbl >= nrb || c0 >= cols) continue;  // whole quads leave together
     const int64_t r0 = (rb0 + rbl) * 32 + 8 * q;
     float p[8][8];
-    load_patch<BF16>(x, ld, r0, c0, p);
-    if (HAD) fwht_columns(p, sign_mask, q);
+    if (HAD) {
+      load_patch_signed<BF16>(x, ld, r0, c0, sign_mask, q, p);
+      fwht_columns(p, q);
+    } else {
+      load_patch<BF16>(x, ld, r0, c0, p);
+    }
 
     uint32_t sb[8];
 #pragma unroll
