@@ -50,6 +50,8 @@ QUANT_CASES = [
     (64, 96, 1, torch.bfloat16),
     (96, 256, 1, torch.float32),
     (40, 544, 1, torch.bfloat16),   # rows not a multiple of 32, ragged chunk tail
+    (72, 160, 1, torch.float32),    # 360 blocks: the last wave of 64 lanes is partial (fp32 pieces)
+    (8, 64, 1, torch.bfloat16),     # 16 blocks: one partial wave
     (64, 96, 0, torch.bfloat16),
     (96, 136, 0, torch.float32),    # cols not a multiple of 128 (ragged lane groups)
     (160, 392, 0, torch.bfloat16),
@@ -89,6 +91,40 @@ def test_quantize_strided_rows(mx, orc, axis):
                           seed=77)
     rc, rs = orc.quantize(hostx(x.contiguous()), axis=axis, scale_rule=1, round_mode=1, hadamard=1,
                           sign_mask=0x12345678, seed=77)
+    assert_bytes_equal(s, rs, "scales")
+    assert_bytes_equal(c, rc, "codes")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_quantize_strided_rows_hadamard_sr(mx, orc, dtype):
+    """ld > cols with row counts that leave partial waves: blocks loaded per lane."""
+    big = special_input(72, 416, dtype, seed=6).to(DEV)
+    x = big[:, 32:352]
+    c, s = mx.mx_quantize(x, axis=1, scale_rule=1, round=1, hadamard=1, sign_mask=0xA5A50F0F,
+                          seed=78)
+    rc, rs = orc.quantize(hostx(x.contiguous()), axis=1, scale_rule=1, round_mode=1, hadamard=1,
+                          sign_mask=0xA5A50F0F, seed=78)
+    assert_bytes_equal(s, rs, "scales")
+    assert_bytes_equal(c, rc, "codes")
+
+
+@pytest.mark.parametrize("axis", [1, 0])
+@pytest.mark.parametrize("rnd", [0, 1])
+def test_hadamard_overflow_block(mx, orc, axis, rnd):
+    """Finite inputs near the fp32 limit whose transform overflows: sums reach infinity, and
+    infinity minus infinity gives NaN in some outputs while others stay finite. The block
+    maximum must see the NaN and infinity outputs exactly as the oracle does."""
+    x = wl.student_t3((64, 96), seed=10)
+    big = 3.0e38
+    x[5, 0:8] = torch.tensor([big, big, big, big, big, big, -big, -big])
+    x[9, 32:40] = torch.tensor([big, big, -big, -big, big, -big, big, -big])
+    x[13, 64:96] = big
+    if axis == 0:
+        x = x.t().contiguous()
+    c, s = mx.mx_quantize(x.to(DEV), axis=axis, scale_rule=1, round=rnd, hadamard=1,
+                          sign_mask=0x0F0F3C3C, seed=91)
+    rc, rs = orc.quantize(hostx(x), axis=axis, scale_rule=1, round_mode=rnd, hadamard=1,
+                          sign_mask=0x0F0F3C3C, seed=91)
     assert_bytes_equal(s, rs, "scales")
     assert_bytes_equal(c, rc, "codes")
 
