@@ -351,6 +351,36 @@ def quant_stream(mx, wl, torch, reps: int = 24, copies: int = 8):
             "quant_stream_8192x4096_pct_of_hbm_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2)}
 
 
+def mfma_ceiling(torch, workgroups: int = 2048, iters: int = 1000, reps: int = 3):
+    """Measured ceiling of the block-scaled FP4 matrix instruction (libmx_probe.so, a measurement
+    aid): one wave per SIMD, 16 independent 32x32x64 accumulator chains per wave, random FP4
+    operand bits and scales near 1, no memory traffic. Returns the median TFLOP/s of `reps`
+    timed launches after one warm-up launch."""
+    import ctypes
+    from mxfp4_block_scaled_hadamard32_amd import build as hip_build
+    if not os.path.exists(hip_build.PROBE_LIB):
+        raise SystemExit("libmx_probe.so is not built (run __graft_entry__.build())")
+    P = ctypes.CDLL(hip_build.PROBE_LIB)
+    P.mx_probe_mfma_fp4.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_uint32,
+                                    ctypes.c_void_p, ctypes.c_void_p]
+    P.mx_probe_mfma_fp4.restype = ctypes.c_int32
+    sink = torch.empty(workgroups * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    rates = []
+    for r in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        rc = P.mx_probe_mfma_fp4(workgroups, iters, 0x9E3779B9 + r, sink.data_ptr(), stream)
+        e1.record()
+        torch.cuda.synchronize()
+        if rc != 0:
+            raise SystemExit(f"mx_probe_mfma_fp4 failed with HIP error {rc}")
+        if r > 0:
+            flops = workgroups * 4 * iters * 16 * 2.0 * 32 * 32 * 64
+            rates.append(flops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    return sorted(rates)[len(rates) // 2]
+
+
 def block_variants(mx, wl, torch, reps: int = 5):
     """Outside the timed step: the tile-size variants on the 2-D workload (W 14336x4096, X
     8192x4096, bf16, ceil scale, RNE): 8x8, 32x32 and 64x64 quantization with both code layouts,
@@ -518,6 +548,7 @@ def main():
     qelems = layer.T * layer.K
     quant_gbs = qelems * QUANT_BYTES_PER_ELEM / (quant_ms * 1e-3) / 1e9
     traffic = load_traffic("wgrad_hbm_bytes_per_launch", args.workload)
+    ceiling = mfma_ceiling(torch)  # after the timed steps, outside the timed region
 
     out = {
         "metric": METRIC,
@@ -551,6 +582,10 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(wgrad_tflops / PEAK_FP4_TFLOPS, 4),
             "traffic": traffic,
+            # the same matrix instruction measured on this GPU with random operand bits and no
+            # memory traffic (clock falls under that power draw): what the kernel could reach
+            "measured_ceiling": round(ceiling, 1),
+            "frac_of_measured_ceiling": round(wgrad_tflops / ceiling, 4),
         },
     }
     if not args.step_only:

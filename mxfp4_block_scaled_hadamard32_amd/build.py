@@ -12,6 +12,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmx.so")
 SOURCES = ["mx_api.hip", "quant.hip", "gemm.hip"]
+# measurement aid for the matrix-core roofline (include/mx_probe.h), a library of its own
+PROBE_LIB = os.path.join(HERE, "libmx_probe.so")
+PROBE_SOURCES = ["mfma_probe.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -26,9 +29,15 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False, extra=()) -> str:
-    tmp = LIB + ".tmp"
+    compile_lib(LIB, SOURCES, verbose, extra)
+    compile_lib(PROBE_LIB, PROBE_SOURCES, verbose, extra)
+    return LIB
+
+
+def compile_lib(lib: str, sources, verbose: bool = False, extra=()) -> str:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), *FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           "-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]
+           "-o", tmp] + [os.path.join(CSRC, s) for s in sources]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -38,8 +47,8 @@ def build(verbose: bool = False, extra=()) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

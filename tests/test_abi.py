@@ -217,3 +217,24 @@ def test_gemm_rejects_operand_tiles_beyond_32_bit_offsets(L):
                            None) == m.MX_ERR_LAUNCH
     assert L.mx_gemm_mxfp8(FAKE, FAKE, 0, FAKE, FAKE, 0, 256, 256, K // 2, 0, 1, FAKE, 256,
                            None) == m.MX_ERR_LAUNCH
+
+
+def test_probe_library_exports_its_declaration():
+    """libmx_probe.so (the matrix-core ceiling probe) exports what include/mx_probe.h declares
+    and rejects bad arguments before any HIP call."""
+    from mxfp4_block_scaled_hadamard32_amd import build as hip_build
+    if not os.path.exists(hip_build.PROBE_LIB):
+        pytest.skip("libmx_probe.so not built (run __graft_entry__.build())")
+    P = ctypes.CDLL(hip_build.PROBE_LIB)
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "mx_probe.h")).read(),
+                  flags=re.S)
+    names = sorted(set(re.findall(r"\b(mx_[a-z0-9_]+)\s*\(", text)))
+    assert names == ["mx_probe_mfma_fp4"]
+    for n in names:
+        assert hasattr(P, n), n
+    f = P.mx_probe_mfma_fp4
+    f.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p]
+    f.restype = ctypes.c_int32
+    assert f(0, 10, 1, FAKE, None) != 0
+    assert f(4, 0, 1, FAKE, None) != 0
+    assert f(4, 10, 1, None, None) != 0
