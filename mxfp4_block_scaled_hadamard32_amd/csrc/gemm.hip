@@ -105,12 +105,12 @@ void gemm_mx_generic_kernel(const uint8_t* __restrict__ A, const uint8_t* __rest
                     void* __restrict__ C, int64_t ldc, int nbm, int nbn) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStageBytes];
 
-  // ---- tile schedule: XCD-contiguous ranges, then groups of 8 tile-rows ----
+  // ---- tile schedule: XCD-contiguous ranges, then groups of 4 tile-rows ----
   const int nblocks = nbm * nbn;
   int bid = blockIdx.x;
   const int per_xcd = nblocks / 8;
   if (bid < per_xcd * 8) bid = (bid % 8) * per_xcd + bid / 8;
-  constexpr int kGroup = 8;
+  constexpr int kGroup = 4;
   const int group = bid / (kGroup * nbn);
   const int first_m = group * kGroup;
   const int gsize = min(nbm - first_m, kGroup);
@@ -401,7 +401,7 @@ void gemm_mx_stream_kernel(const uint8_t* __restrict__ A, const uint8_t* __restr
   int bid = blockIdx.x;
   const int per_xcd = nblocks / 8;
   if (bid < per_xcd * 8) bid = (bid % 8) * per_xcd + bid / 8;
-  constexpr int kGroup = 8;
+  constexpr int kGroup = 4;
   const int group = bid / (kGroup * nbn);
   const int first_m = group * kGroup;
   const int gsize = min(nbm - first_m, kGroup);
@@ -850,8 +850,11 @@ void gemm_mx_stream_kernel(const uint8_t* __restrict__ A, const uint8_t* __restr
       const int r = 2 * (q * WAVES + wave) + fhalf;
       const u32x4 v = *reinterpret_cast<const u32x4*>(smem + r * kPitch + 16 * frow);
       const int64_t m = m0 + r, n = n0 + 8 * frow;
+      // non-temporal: the output streams past L2 instead of displacing the operand panels the
+      // XCD's other tiles are still reading there
       if (full || (m < M && n < N))
-        *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(C) + m * ldc + n) = v;
+        __builtin_nontemporal_store(
+            v, reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(C) + m * ldc + n));
     }
   } else {
     // fp32: two passes of 128 rows (the waves with wm == p fill pass p)
@@ -884,7 +887,8 @@ void gemm_mx_stream_kernel(const uint8_t* __restrict__ A, const uint8_t* __restr
         const f32x4 v = *reinterpret_cast<const f32x4*>(smem + r * kPitch + 16 * lane);
         const int64_t m = m0 + p * kPassRows + r, n = n0 + 4 * lane;
         if (full || (m < M && n < N))
-          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(C) + m * ldc + n) = v;
+          __builtin_nontemporal_store(
+              v, reinterpret_cast<f32x4*>(reinterpret_cast<float*>(C) + m * ldc + n));
       }
       if (p == 0) {
         __builtin_amdgcn_s_waitcnt(0xC07F);
