@@ -13,10 +13,13 @@
 //  [P4] "Training LLMs with MXFP4", abstract: random Hadamard signs with stochastic rounding.
 //
 // Work mapping (all kernels are HBM streams):
-//  * A lane owns 8 consecutive elements of a row (one 16-byte bf16 load). Along rows, a quad of
-//    4 lanes holds one 32-block: butterfly spans 1, 2, 4 stay in the lane, spans 8 and 16 use
-//    DPP quad permutes; the block maximum reduces the same way.
-//  * Along columns and for 32x32 tiles, a lane owns an 8x8 patch (8 rows of 16 bytes). A quad
+//  * Along rows (MXFP4), a lane owns one whole 32-block: all five butterfly stages, the block
+//    maximum and the scale stay in its registers. Loads are coalesced across the wave and
+//    regrouped per block through the wave's LDS area.
+//  * Along rows (MXFP8), a lane owns 8 consecutive elements (one 16-byte bf16 load) and a quad
+//    of 4 lanes holds a block: butterfly spans 1, 2, 4 stay in the lane, spans 8 and 16 use DPP
+//    quad permutes; the block maximum reduces the same way.
+//  * Along columns and for square tiles, a lane owns an 8x8 patch (8 rows of 16 bytes). A quad
 //    stacks 4 patches into 32 rows, so the same in-lane + quad structure runs down the columns;
 //    16 lanes (4 quads side by side) make one 32x32 tile.
 //  * Stochastic rounding draws one Philox4x32-10 call per 8 consecutive source elements.
