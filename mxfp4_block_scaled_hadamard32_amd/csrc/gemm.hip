@@ -360,6 +360,14 @@ struct StreamCfg {
   static constexpr int kScaleLoads = kGroupScales ? kGroupLoads
                                                   : 2 * (kBM * kScaleRow / 256) / WAVES;
   static constexpr int kLoads = 2 * kCodeLoads + kScaleLoads;
+  // FP4 scale groups (32-byte rows, two 16-byte halves of two steps each): row r keeps its
+  // halves swapped when bit 3 of r is set. A step's scale reads hit 32 consecutive rows at one
+  // offset; with plain 32-byte rows every 8th row shares a bank (4-way conflicts), with the swap
+  // rows r and r + 8 use different banks (2-way), and each direct load still moves whole halves.
+  static constexpr bool kScaleSwap = kGroupScales && kGroupRow == 32;
+  __device__ static __forceinline__ int scale_swap(int row) {
+    return kScaleSwap ? ((row >> 3) & 1) << 4 : 0;
+  }
   static constexpr int kSwzShift = BKS == 2 ? 2 : 1;            // rows sharing a bank phase
   // byte offset of 16-byte chunk `chunk` of row `row` in a stage's code tile: the chunk
   // position is XOR-ed with a row phase so that 16 consecutive rows hit distinct bank groups
@@ -458,8 +466,8 @@ void gemm_mx_stream_kernel(const uint8_t* __restrict__ A, const uint8_t* __restr
   // group mode: quarter p of a group holds rows 128 p .. 128 p + 127 of the 512 scale rows
   // (A rows 0-255, then B), 32 bytes each. Load h of wave w covers bytes
   // (w G + h) 64 LB .. +64 LB of the quarter (G loads per wave, LB bytes per lane), so lane l
-  // fetches byte (q % 32) of row 128 p + q / 32 for q = ((w G + h) 64 + l) LB. Quarters 0-1 are
-  // A rows, 2-3 are B rows, so the operand depends on p only.
+  // fetches byte (q % 32) ^ scale_swap(row) of row 128 p + q / 32 for q = ((w G + h) 64 + l) LB.
+  // Quarters 0-1 are A rows, 2-3 are B rows, so the operand depends on p only.
   constexpr int kGL = Cfg::kGroupLoads, kLB = Cfg::kGroupLaneBytes;
   int goff[4][Cfg::kGroupScales ? kGL : 1];
   if constexpr (Cfg::kGroupScales) {
@@ -469,7 +477,7 @@ void gemm_mx_stream_kernel(const uint8_t* __restrict__ A, const uint8_t* __restr
       for (int h = 0; h < kGL; ++h) {
         const int q = ((wave * kGL + h) * 64 + lane) * kLB;
         const int row = (128 * p + q / Cfg::kGroupRow) & (kBM - 1);
-        const int byte = q % Cfg::kGroupRow;
+        const int byte = (q % Cfg::kGroupRow) ^ Cfg::scale_swap(row);
         if (p < 2)
           goff[p][h] = row < rows_a ? (int)((((m0 + row) >> lga) - s0a) * nkb) + byte : (int)sbytes_a;
         else
@@ -540,8 +548,9 @@ void gemm_mx_stream_kernel(const uint8_t* __restrict__ A, const uint8_t* __restr
     const uint32_t* pb;
     int stride;  // words per row
     if constexpr (Cfg::kGroupScales) {
-      const uint8_t* gb = sgroup + ((ks / Cfg::kGroupSteps) & 1) * Cfg::kGroupBytes +
-                          (ks % Cfg::kGroupSteps) * Cfg::kScaleRow;
+      // rows wm * 32 FA + 32 i + frow all have bit 3 of frow, so the half swap is per lane
+      const int soff = ((ks % Cfg::kGroupSteps) * Cfg::kScaleRow) ^ Cfg::scale_swap(frow);
+      const uint8_t* gb = sgroup + ((ks / Cfg::kGroupSteps) & 1) * Cfg::kGroupBytes + soff;
       pa = reinterpret_cast<const uint32_t*>(gb);
       pb = reinterpret_cast<const uint32_t*>(gb + kBM * Cfg::kGroupRow);
       stride = Cfg::kGroupRow / 4;
