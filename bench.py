@@ -437,26 +437,33 @@ COPY_BYTES = 1 << 30  # the --copy-calibration copy reads and writes 1 GiB
 
 def counter_values(path: str, counter: str):
     """Per-dispatch values of `counter` from a rocprofv3 counter_collection.csv (summed over the
-    hardware instances of each dispatch), grouped by (kernel name, workgroup count)."""
+    hardware instances of each dispatch), as {kernel name: [values in dispatch order]}."""
     import collections
     import csv
     per = collections.defaultdict(float)
-    key_of = {}
+    name_of = {}
     for r in csv.DictReader(open(path)):
         if r["Counter_Name"] != counter:
             continue
         d = int(r["Dispatch_Id"])
         per[d] += float(r["Counter_Value"])
-        key_of[d] = (r["Kernel_Name"], int(r["Grid_Size"]) // max(int(r["Workgroup_Size"]), 1))
+        name_of[d] = r["Kernel_Name"]
     out = collections.defaultdict(list)
-    for d, v in per.items():
-        out[key_of[d]].append(v)
+    for d in sorted(per):
+        out[name_of[d]].append(per[d])
     return out
+
+
+# the counter passes run 1 warm-up + 2 timed steps, each launching Fprop, Dgrad, Wgrad in turn
+TRAFFIC_STEPS = 3
+TRAFFIC_ORDER = ("fprop", "dgrad", "wgrad")
 
 
 def write_traffic(fetch_csv: str, write_csv: str, workload: str):
     """HBM bytes per launch of each GEMM from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each
-    scaled by what the same counter reads for the plain 1 GiB copy of the calibration run."""
+    scaled by what the same counter reads for the plain 1 GiB copy of the calibration run. The
+    GEMM runs on a resident grid (the same workgroup count for every shape), so the launches are
+    told apart by their order in the step; the bf16 output bytes each launch writes confirm it."""
     if workload != "llama70b_down":
         raise SystemExit("traffic records are kept for the llama70b_down workload")
     T, K, N = 16384, 28672, 8192  # tokens, FFN (Fprop reduction), hidden
@@ -464,7 +471,7 @@ def write_traffic(fetch_csv: str, write_csv: str, workload: str):
 
     def copy_value(table):
         # the calibration copy is the largest device-to-device copy dispatch of the run
-        vals = [v for (name, _), vs in table.items() if "copyBuffer" in name for v in vs]
+        vals = [v for name, vs in table.items() if "copyBuffer" in name for v in vs]
         if not vals:
             raise SystemExit("no copy kernel in the counter file (run with --copy-calibration)")
         return max(vals)
@@ -472,15 +479,24 @@ def write_traffic(fetch_csv: str, write_csv: str, workload: str):
     ff = COPY_BYTES / (copy_value(fetch) * 1024.0)
     wf = COPY_BYTES / (copy_value(write) * 1024.0)
 
-    def gemm_value(table, wgs):
-        # the MXFP4 GEMM with plain output (template arguments ..., QOUT false, A and B
-        # formats 4), not the quantizing epilogue or the MXFP8 kernel
-        vals = [vs for (name, g), vs in table.items()
-                if re.search(r"gemm_mx\w*<[^>]*false, 4, 4>", name) and g == wgs]
-        if len(vals) != 1:
-            raise SystemExit(f"expected one GEMM kernel with {wgs} workgroups, found {len(vals)}")
-        return sum(vals[0]) / len(vals[0])
+    def gemm_launches(table):
+        # the MXFP4 GEMM with plain output (template arguments ..., QOUT false, A and B formats
+        # 4), not the quantizing epilogue or the MXFP8 kernel; the step's launches come first
+        vals = [vs for name, vs in table.items() if re.search(r"gemm_mx\w*<[^>]*false, 4, 4>", name)]
+        if len(vals) != 1 or len(vals[0]) < 3 * TRAFFIC_STEPS:
+            raise SystemExit("expected one MXFP4 GEMM kernel with the step's launches first")
+        per = {k: [] for k in TRAFFIC_ORDER}
+        for i, v in enumerate(vals[0][:3 * TRAFFIC_STEPS]):
+            per[TRAFFIC_ORDER[i % 3]].append(v)
+        return per
 
+    shapes = {"fprop": (T, N, K), "dgrad": (T, K, N), "wgrad": (N, K, T)}
+    fetch_l, write_l = gemm_launches(fetch), gemm_launches(write)
+    for name, (M, Nn, Kk) in shapes.items():
+        out_bytes = 2 * M * Nn
+        got = sum(write_l[name]) / len(write_l[name]) * 1024.0 * wf
+        if abs(got - out_bytes) > 0.08 * out_bytes:  # beyond C: register spill traffic
+            raise SystemExit(f"{name}: launch writes {got:.3e} B, expected its bf16 output {out_bytes:.3e} B")
     rec = {"gemm_sha": sha(GEMM_SRC), "fetch_factor": ff, "write_factor": wf,
            "command_fetch": ("rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch "
                              "-o run -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline "
@@ -488,9 +504,10 @@ def write_traffic(fetch_csv: str, write_csv: str, workload: str):
            "command_write": ("rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write "
                              "-o run -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline "
                              "--step-only --with-variants --copy-calibration")}
-    for name, M, Nn, Kk in (("fprop", T, N, K), ("dgrad", T, K, N), ("wgrad", N, K, T)):
-        wgs = ((M + 255) // 256) * ((Nn + 255) // 256)
-        hbm = gemm_value(fetch, wgs) * 1024.0 * ff + gemm_value(write, wgs) * 1024.0 * wf
+    for name, (M, Nn, Kk) in shapes.items():
+        fv = sum(fetch_l[name]) / len(fetch_l[name])
+        wv = sum(write_l[name]) / len(write_l[name])
+        hbm = fv * 1024.0 * ff + wv * 1024.0 * wf
         alg = (M + Nn) * (Kk // 2 + Kk // 32) + 2 * M * Nn  # both operands with scales + bf16 C
         rec[f"{name}_hbm_bytes_per_launch"] = int(round(hbm))
         rec[f"{name}_algorithmic_bytes_per_launch"] = int(alg)

@@ -406,508 +406,530 @@ void gemm_mx_stream_kernel(const uint8_t* __restrict__ A, const uint8_t* __restr
   uint8_t* const sgroup = smem + STAGES * Cfg::kStage;  // scale groups (BKS == 4)
 
   const int nblocks = nbm * nbn;
-  int bid = blockIdx.x;
-  const int per_xcd = nblocks / 8;
-  if (bid < per_xcd * 8) bid = (bid % 8) * per_xcd + bid / 8;
-  constexpr int kGroup = 4;
-  const int group = bid / (kGroup * nbn);
-  const int first_m = group * kGroup;
-  const int gsize = min(nbm - first_m, kGroup);
-  const int in_group = bid - group * kGroup * nbn;
-  const int tm = first_m + in_group % gsize;
-  const int tn = in_group / gsize;
-  const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
+  // Tiles blockIdx.x, blockIdx.x + gridDim.x, ...: a resident grid (one workgroup per CU, a
+  // multiple of 8, so tile t stays on XCD t % 8 as the ordering below assumes) walks the tiles
+  // in the same order as a grid of one workgroup per tile, without a dispatch gap between them.
+  for (int tile = blockIdx.x; tile < nblocks; tile += gridDim.x) {
+    int bid = tile;
+    const int per_xcd = nblocks / 8;
+    if (bid < per_xcd * 8) bid = (bid % 8) * per_xcd + bid / 8;
+    constexpr int kGroup = 4;
+    const int group = bid / (kGroup * nbn);
+    const int first_m = group * kGroup;
+    const int gsize = min(nbm - first_m, kGroup);
+    const int in_group = bid - group * kGroup * nbn;
+    const int tm = first_m + in_group % gsize;
+    const int tn = in_group / gsize;
+    const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
 
-  const int t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
-  const int wm = wave % WM, wn = wave / WM;
-  const int64_t kbytes = F8 ? K : K / 2, nkb = K / 32;
-  const int nk = (int)(K / Cfg::kKStage);
-  const int frow = lane & 31, fhalf = lane >> 5;
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));  // per tile: keep lane setup out of the loop-carried state
+    const int lane = t & 63, wave = t >> 6;
+    const int wm = wave % WM, wn = wave / WM;
+    const int64_t kbytes = F8 ? K : K / 2, nkb = K / 32;
+    const int nk = (int)(K / Cfg::kKStage);
+    const int frow = lane & 31, fhalf = lane >> 5;
 
-  const int64_t rows_a = min((int64_t)kBM, M - m0), rows_b = min((int64_t)kBN, N - n0);
-  const i32x4 ra = rsrc_words(A + m0 * kbytes, rows_a * kbytes);
-  const i32x4 rb = rsrc_words(B + n0 * kbytes, rows_b * kbytes);
-  const int64_t s0a = m0 >> lga, s0b = n0 >> lgb;
-  const int64_t sbytes_a = (((m0 + rows_a - 1) >> lga) - s0a + 1) * nkb;
-  const int64_t sbytes_b = (((n0 + rows_b - 1) >> lgb) - s0b + 1) * nkb;
-  const i32x4 rsa = rsrc_words(As + s0a * nkb, sbytes_a);
-  const i32x4 rsb = rsrc_words(Bs + s0b * nkb, sbytes_b);
+    const int64_t rows_a = min((int64_t)kBM, M - m0), rows_b = min((int64_t)kBN, N - n0);
+    const i32x4 ra = rsrc_words(A + m0 * kbytes, rows_a * kbytes);
+    const i32x4 rb = rsrc_words(B + n0 * kbytes, rows_b * kbytes);
+    const int64_t s0a = m0 >> lga, s0b = n0 >> lgb;
+    const int64_t sbytes_a = (((m0 + rows_a - 1) >> lga) - s0a + 1) * nkb;
+    const int64_t sbytes_b = (((n0 + rows_b - 1) >> lgb) - s0b + 1) * nkb;
+    const i32x4 rsa = rsrc_words(As + s0a * nkb, sbytes_a);
+    const i32x4 rsb = rsrc_words(Bs + s0b * nkb, sbytes_b);
 
-  // code load i of this wave fills 1 KiB block b = i * WAVES + wave of the tile: rows
-  // kRowsPerBlock * b + lane / (2 BKS), position lane % (2 BKS), i.e. chunk position ^ phase
-  int voff[Cfg::kCodeLoads];
-#pragma unroll
-  for (int i = 0; i < Cfg::kCodeLoads; ++i) {
-    const int b = i * WAVES + wave;
-    const int row = Cfg::kRowsPerBlock * b + lane / (2 * BKS);
-    const int pos = lane % (2 * BKS);
-    const int chunk = pos ^ ((row >> Cfg::kSwzShift) & (2 * BKS - 1));
-    voff[i] = (int)(row * kbytes) + 16 * chunk;
-  }
-  // scale load j of this wave: 256-byte piece q of operand o (rows of 2 BKS bytes, lane ->
-  // row piece * (128 / BKS) + lane / SW, word lane % SW); rows past the operand read zero
-  constexpr int kPieces = kBM * Cfg::kScaleRow / 256;  // per operand
-  int soff[Cfg::kGroupScales ? 1 : Cfg::kScaleLoads];
-  if constexpr (!Cfg::kGroupScales) {
-    if constexpr (!Cfg::kGroupScales)
-#pragma unroll
-    for (int j = 0; j < Cfg::kScaleLoads; ++j) {
-      const int sidx = wave + j * WAVES;
-      const int o = sidx / kPieces, q = sidx % kPieces;
-      const int row = q * (128 / BKS) + lane / SW;
-      const int word = lane % SW;
-      if (o == 0)
-        soff[j] = row < rows_a ? (int)((((m0 + row) >> lga) - s0a) * nkb) + 4 * word : (int)sbytes_a;
-      else
-        soff[j] = row < rows_b ? (int)((((n0 + row) >> lgb) - s0b) * nkb) + 4 * word : (int)sbytes_b;
-    }
-  }
-  // group mode: quarter p of a group holds rows 128 p .. 128 p + 127 of the 512 scale rows
-  // (A rows 0-255, then B), 32 bytes each. Load h of wave w covers bytes
-  // (w G + h) 64 LB .. +64 LB of the quarter (G loads per wave, LB bytes per lane), so lane l
-  // fetches byte (q % 32) ^ scale_swap(row) of row 128 p + q / 32 for q = ((w G + h) 64 + l) LB.
-  // Quarters 0-1 are A rows, 2-3 are B rows, so the operand depends on p only.
-  constexpr int kGL = Cfg::kGroupLoads, kLB = Cfg::kGroupLaneBytes;
-  int goff[4][Cfg::kGroupScales ? kGL : 1];
-  if constexpr (Cfg::kGroupScales) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p)
-#pragma unroll
-      for (int h = 0; h < kGL; ++h) {
-        const int q = ((wave * kGL + h) * 64 + lane) * kLB;
-        const int row = (128 * p + q / Cfg::kGroupRow) & (kBM - 1);
-        const int byte = (q % Cfg::kGroupRow) ^ Cfg::scale_swap(row);
-        if (p < 2)
-          goff[p][h] = row < rows_a ? (int)((((m0 + row) >> lga) - s0a) * nkb) + byte : (int)sbytes_a;
-        else
-          goff[p][h] = row < rows_b ? (int)((((n0 + row) >> lgb) - s0b) * nkb) + byte : (int)sbytes_b;
-      }
-  }
-  const int ngroups = (nk + Cfg::kGroupSteps - 1) / Cfg::kGroupSteps;
-  // load h of quarter p of scale group g into buffer g % 2 (groups past the end re-read the
-  // last one)
-  auto issue_group_load = [&](int g, int p, int h) {
-    const int gs = min(g, ngroups - 1);
-    const uint32_t dst = lds_addr(sgroup + (g & 1) * Cfg::kGroupBytes + 128 * p * Cfg::kGroupRow +
-                                  (wave * kGL + h) * 64 * kLB);
-    const i32x4 sel = p < 2 ? rsa : rsb;
-    if constexpr (kLB == 16) dma_b128(sel, dst, goff[p][h], gs * Cfg::kGroupRow);
-    else dma_b32(sel, dst, goff[p][h], gs * Cfg::kGroupRow);
-  };
-  auto issue_group_part = [&](int g, int p) {
-#pragma unroll
-    for (int h = 0; h < kGL; ++h) issue_group_load(g, p, h);
-  };
-
-  auto stage_ptr = [&](int st) { return smem + st * Cfg::kStage; };
-  auto issue = [&](uint8_t* st, int ks) {
-    const int kofs = ks * Cfg::kRow;
+    // code load i of this wave fills 1 KiB block b = i * WAVES + wave of the tile: rows
+    // kRowsPerBlock * b + lane / (2 BKS), position lane % (2 BKS), i.e. chunk position ^ phase
+    int voff[Cfg::kCodeLoads];
 #pragma unroll
     for (int i = 0; i < Cfg::kCodeLoads; ++i) {
-      const uint32_t dst = lds_addr(st + 1024 * (i * WAVES + wave));
-      dma_b128(ra, dst, voff[i], kofs);
-      dma_b128(rb, dst + Cfg::kTile, voff[i], kofs);
+      const int b = i * WAVES + wave;
+      const int row = Cfg::kRowsPerBlock * b + lane / (2 * BKS);
+      const int pos = lane % (2 * BKS);
+      const int chunk = pos ^ ((row >> Cfg::kSwzShift) & (2 * BKS - 1));
+      voff[i] = (int)(row * kbytes) + 16 * chunk;
     }
-    if constexpr (!Cfg::kGroupScales)
+    // scale load j of this wave: 256-byte piece q of operand o (rows of 2 BKS bytes, lane ->
+    // row piece * (128 / BKS) + lane / SW, word lane % SW); rows past the operand read zero
+    constexpr int kPieces = kBM * Cfg::kScaleRow / 256;  // per operand
+    int soff[Cfg::kGroupScales ? 1 : Cfg::kScaleLoads];
+    if constexpr (!Cfg::kGroupScales) {
+      if constexpr (!Cfg::kGroupScales)
 #pragma unroll
-    for (int j = 0; j < Cfg::kScaleLoads; ++j) {
-      const int sidx = wave + j * WAVES;
-      const int o = sidx / kPieces, q = sidx % kPieces;
-      const uint32_t dst = lds_addr(st + 2 * Cfg::kTile + o * kBM * Cfg::kScaleRow + 256 * q);
-      const i32x4 sel = o == 0 ? rsa : rsb;  // wave-uniform; pin it to scalar registers
-      const i32x4 rs = {__builtin_amdgcn_readfirstlane(sel.x), __builtin_amdgcn_readfirstlane(sel.y),
-                        __builtin_amdgcn_readfirstlane(sel.z), __builtin_amdgcn_readfirstlane(sel.w)};
-      dma_b32(rs, dst, soff[j], ks * Cfg::kScaleRow);
+      for (int j = 0; j < Cfg::kScaleLoads; ++j) {
+        const int sidx = wave + j * WAVES;
+        const int o = sidx / kPieces, q = sidx % kPieces;
+        const int row = q * (128 / BKS) + lane / SW;
+        const int word = lane % SW;
+        if (o == 0)
+          soff[j] = row < rows_a ? (int)((((m0 + row) >> lga) - s0a) * nkb) + 4 * word : (int)sbytes_a;
+        else
+          soff[j] = row < rows_b ? (int)((((n0 + row) >> lgb) - s0b) * nkb) + 4 * word : (int)sbytes_b;
+      }
     }
-  };
-  // a lane's fragment of sub-step sub (64 k values of one row): FP4, the 32 values of k-block
-  // fhalf (16 bytes, chunk 2 sub + fhalf); FP8, 16 values of each k-block, the half fhalf of
-  // block 0 in bytes 0-15 and of block 1 in bytes 16-31 (chunks 4 sub + fhalf and
-  // 4 sub + 2 + fhalf)
-  auto frag = [&](const uint8_t* tile, int row, int sub) -> Frag {
-    if constexpr (F8) {
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(tile + Cfg::swz(row, 4 * sub + fhalf));
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(tile + Cfg::swz(row, 4 * sub + 2 + fhalf));
-      return u32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    } else {
-      return *reinterpret_cast<const u32x4*>(tile + Cfg::swz(row, 2 * sub + fhalf));
-    }
-  };
-  auto lread = [&](const uint8_t* st, int sub, Frag (&fa)[FA], Frag (&fb)[FB]) {
-#pragma unroll
-    for (int i = 0; i < FA; ++i) fa[i] = frag(st, wm * 32 * FA + 32 * i + frow, sub);
-#pragma unroll
-    for (int j = 0; j < FB; ++j) fb[j] = frag(st + Cfg::kTile, wn * 32 * FB + 32 * j + frow, sub);
-  };
-  // per-lane scale words of a stage: word w holds k-blocks 4w..4w+3 of the row; lanes 0-31
-  // use the even blocks, lanes 32-63 the odd ones, so shift by one byte on the upper half and
-  // let op_sel 0 / 2 pick sub-step 2w / 2w+1
-  auto sread = [&](const uint8_t* st, int ks, uint32_t (&sa)[FA][SW], uint32_t (&sb)[FB][SW]) {
-    const uint32_t* pa;
-    const uint32_t* pb;
-    int stride;  // words per row
+    // group mode: quarter p of a group holds rows 128 p .. 128 p + 127 of the 512 scale rows
+    // (A rows 0-255, then B), 32 bytes each. Load h of wave w covers bytes
+    // (w G + h) 64 LB .. +64 LB of the quarter (G loads per wave, LB bytes per lane), so lane l
+    // fetches byte (q % 32) ^ scale_swap(row) of row 128 p + q / 32 for q = ((w G + h) 64 + l) LB.
+    // Quarters 0-1 are A rows, 2-3 are B rows, so the operand depends on p only.
+    constexpr int kGL = Cfg::kGroupLoads, kLB = Cfg::kGroupLaneBytes;
+    int goff[4][Cfg::kGroupScales ? kGL : 1];
     if constexpr (Cfg::kGroupScales) {
-      // rows wm * 32 FA + 32 i + frow all have bit 3 of frow, so the half swap is per lane
-      const int soff = ((ks % Cfg::kGroupSteps) * Cfg::kScaleRow) ^ Cfg::scale_swap(frow);
-      const uint8_t* gb = sgroup + ((ks / Cfg::kGroupSteps) & 1) * Cfg::kGroupBytes + soff;
-      pa = reinterpret_cast<const uint32_t*>(gb);
-      pb = reinterpret_cast<const uint32_t*>(gb + kBM * Cfg::kGroupRow);
-      stride = Cfg::kGroupRow / 4;
-    } else {
-      pa = reinterpret_cast<const uint32_t*>(st + 2 * Cfg::kTile);
-      pb = reinterpret_cast<const uint32_t*>(st + 2 * Cfg::kTile + kBM * Cfg::kScaleRow);
-      stride = SW;
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+#pragma unroll
+        for (int h = 0; h < kGL; ++h) {
+          const int q = ((wave * kGL + h) * 64 + lane) * kLB;
+          const int row = (128 * p + q / Cfg::kGroupRow) & (kBM - 1);
+          const int byte = (q % Cfg::kGroupRow) ^ Cfg::scale_swap(row);
+          if (p < 2)
+            goff[p][h] = row < rows_a ? (int)((((m0 + row) >> lga) - s0a) * nkb) + byte : (int)sbytes_a;
+          else
+            goff[p][h] = row < rows_b ? (int)((((n0 + row) >> lgb) - s0b) * nkb) + byte : (int)sbytes_b;
+        }
     }
+    const int ngroups = (nk + Cfg::kGroupSteps - 1) / Cfg::kGroupSteps;
+    // load h of quarter p of scale group g into buffer g % 2 (groups past the end re-read the
+    // last one)
+    auto issue_group_load = [&](int g, int p, int h) {
+      const int gs = min(g, ngroups - 1);
+      const uint32_t dst = lds_addr(sgroup + (g & 1) * Cfg::kGroupBytes + 128 * p * Cfg::kGroupRow +
+                                    (wave * kGL + h) * 64 * kLB);
+      const i32x4 sel = p < 2 ? rsa : rsb;
+      if constexpr (kLB == 16) dma_b128(sel, dst, goff[p][h], gs * Cfg::kGroupRow);
+      else dma_b32(sel, dst, goff[p][h], gs * Cfg::kGroupRow);
+    };
+    auto issue_group_part = [&](int g, int p) {
 #pragma unroll
-    for (int i = 0; i < FA; ++i)
-#pragma unroll
-      for (int w = 0; w < SW; ++w) sa[i][w] = pa[(wm * 32 * FA + 32 * i + frow) * stride + w] >> (8 * fhalf);
-#pragma unroll
-    for (int j = 0; j < FB; ++j)
-#pragma unroll
-      for (int w = 0; w < SW; ++w) sb[j][w] = pb[(wn * 32 * FB + 32 * j + frow) * stride + w] >> (8 * fhalf);
-  };
+      for (int h = 0; h < kGL; ++h) issue_group_load(g, p, h);
+    };
 
-  v16f acc[FA][FB];
+    auto stage_ptr = [&](int st) { return smem + st * Cfg::kStage; };
+    auto issue = [&](uint8_t* st, int ks) {
+      const int kofs = ks * Cfg::kRow;
 #pragma unroll
-  for (int i = 0; i < FA; ++i)
+      for (int i = 0; i < Cfg::kCodeLoads; ++i) {
+        const uint32_t dst = lds_addr(st + 1024 * (i * WAVES + wave));
+        dma_b128(ra, dst, voff[i], kofs);
+        dma_b128(rb, dst + Cfg::kTile, voff[i], kofs);
+      }
+      if constexpr (!Cfg::kGroupScales)
 #pragma unroll
-    for (int j = 0; j < FB; ++j)
+      for (int j = 0; j < Cfg::kScaleLoads; ++j) {
+        const int sidx = wave + j * WAVES;
+        const int o = sidx / kPieces, q = sidx % kPieces;
+        const uint32_t dst = lds_addr(st + 2 * Cfg::kTile + o * kBM * Cfg::kScaleRow + 256 * q);
+        const i32x4 sel = o == 0 ? rsa : rsb;  // wave-uniform; pin it to scalar registers
+        const i32x4 rs = {__builtin_amdgcn_readfirstlane(sel.x), __builtin_amdgcn_readfirstlane(sel.y),
+                          __builtin_amdgcn_readfirstlane(sel.z), __builtin_amdgcn_readfirstlane(sel.w)};
+        dma_b32(rs, dst, soff[j], ks * Cfg::kScaleRow);
+      }
+    };
+    // a lane's fragment of sub-step sub (64 k values of one row): FP4, the 32 values of k-block
+    // fhalf (16 bytes, chunk 2 sub + fhalf); FP8, 16 values of each k-block, the half fhalf of
+    // block 0 in bytes 0-15 and of block 1 in bytes 16-31 (chunks 4 sub + fhalf and
+    // 4 sub + 2 + fhalf)
+    auto frag = [&](const uint8_t* tile, int row, int sub) -> Frag {
+      if constexpr (F8) {
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(tile + Cfg::swz(row, 4 * sub + fhalf));
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(tile + Cfg::swz(row, 4 * sub + 2 + fhalf));
+        return u32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      } else {
+        return *reinterpret_cast<const u32x4*>(tile + Cfg::swz(row, 2 * sub + fhalf));
+      }
+    };
+    auto lread = [&](const uint8_t* st, int sub, Frag (&fa)[FA], Frag (&fb)[FB]) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-  // MFMAs of sub-step SUB: scale word SUB / 2, byte pair selected by op_sel 2 * (SUB % 2)
-  auto mma = [&](const Frag (&fa)[FA], const Frag (&fb)[FB], const uint32_t (&sa)[FA][SW],
-                 const uint32_t (&sb)[FB][SW], auto sub) {
-    constexpr int SUB = decltype(sub)::value;
-    constexpr int OP = 2 * (SUB % 2), W = SUB / 2;
+      for (int i = 0; i < FA; ++i) fa[i] = frag(st, wm * 32 * FA + 32 * i + frow, sub);
 #pragma unroll
-    for (int i = 0; i < FA; ++i)
+      for (int j = 0; j < FB; ++j) fb[j] = frag(st + Cfg::kTile, wn * 32 * FB + 32 * j + frow, sub);
+    };
+    // per-lane scale words of a stage: word w holds k-blocks 4w..4w+3 of the row; lanes 0-31
+    // use the even blocks, lanes 32-63 the odd ones, so shift by one byte on the upper half and
+    // let op_sel 0 / 2 pick sub-step 2w / 2w+1
+    auto sread = [&](const uint8_t* st, int ks, uint32_t (&sa)[FA][SW], uint32_t (&sb)[FB][SW]) {
+      const uint32_t* pa;
+      const uint32_t* pb;
+      int stride;  // words per row
+      if constexpr (Cfg::kGroupScales) {
+        // rows wm * 32 FA + 32 i + frow all have bit 3 of frow, so the half swap is per lane
+        const int soff = ((ks % Cfg::kGroupSteps) * Cfg::kScaleRow) ^ Cfg::scale_swap(frow);
+        const uint8_t* gb = sgroup + ((ks / Cfg::kGroupSteps) & 1) * Cfg::kGroupBytes + soff;
+        pa = reinterpret_cast<const uint32_t*>(gb);
+        pb = reinterpret_cast<const uint32_t*>(gb + kBM * Cfg::kGroupRow);
+        stride = Cfg::kGroupRow / 4;
+      } else {
+        pa = reinterpret_cast<const uint32_t*>(st + 2 * Cfg::kTile);
+        pb = reinterpret_cast<const uint32_t*>(st + 2 * Cfg::kTile + kBM * Cfg::kScaleRow);
+        stride = SW;
+      }
+#pragma unroll
+      for (int i = 0; i < FA; ++i)
+#pragma unroll
+        for (int w = 0; w < SW; ++w) sa[i][w] = pa[(wm * 32 * FA + 32 * i + frow) * stride + w] >> (8 * fhalf);
 #pragma unroll
       for (int j = 0; j < FB; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            as_operand(fb[j]), as_operand(fa[i]), acc[i][j], BF, AF, OP, sb[j][W], OP, sa[i][W]);
-  };
+#pragma unroll
+        for (int w = 0; w < SW; ++w) sb[j][w] = pb[(wn * 32 * FB + 32 * j + frow) * stride + w] >> (8 * fhalf);
+    };
 
-  Frag fa0[FA], fb0[FB], fa1[FA], fb1[FB];
-  uint32_t saC[FA][SW], sbC[FB][SW], saN[FA][SW], sbN[FB][SW];
-
-  // Every step issues exactly LOADS loads per wave (steps past the end re-read step nk-1 into
-  // a stage nobody reads again), so each wait is a constant count and the loop has no branches.
-  auto issue_step = [&](uint8_t* st, int ks) { issue(st, min(ks, nk - 1)); };
-
-  // Group mode schedule: the load bundle of step j (its code loads, issued two steps ahead)
-  // also carries quarter (j + 3) % 4 of scale group (j + 3) / 4, so group G arrives with the
-  // bundles of steps 4G-3 .. 4G. That makes it complete (loads retire in order) when the
-  // scales of step 4G are first read, at the barrier of step 4G-1, and its first quarter is
-  // requested only after the barrier of step 4G-5, after which nobody reads the previous
-  // occupant of its buffer (group G-2) any more. Quarters 0-2 of group 0 go out on their own.
-  auto issue_bundle = [&](uint8_t* st, int j) {
-    issue_step(st, j);
-    if constexpr (Cfg::kGroupScales) issue_group_part((j + 3) / 4, (j + 3) % 4);
-  };
-  // Spread schedule (2 stages): load L of bundle j (L < S: load L of its scale quarter, S the
-  // number of scale loads per step; L = S + q: code load q / 2 of operand q % 2) is issued
-  // between MFMAs instead of in one burst after the
-  // barrier, so that a full address queue stalls a single load rather than the whole sub-step.
-  // Loads 0 .. kP3-1 go out during the last sub-step of step j-2 (right after its barrier),
-  // the rest during sub-steps 0 .. 2 of step j-1; all of them land by the barrier of step j-1.
-  // FP4: at most one load per pair of MFMAs; FP8 (MFMAs twice as long): one per MFMA
-  constexpr int kPer = F8 ? 1 : 2;
-  constexpr int kP3 = SPLIT3, kP0 = SPLIT0, kP1 = SPLIT1, kP2 = LOADS - kP3 - kP0 - kP1;
-  static_assert(STAGES != 2 || (kP2 >= 0 && kPer * kP3 <= FA * FB && kPer * kP0 <= FA * FB &&
-                kPer * kP1 <= FA * FB && kPer * kP2 <= FA * FB), "loads per sub-step");
-  static_assert(STAGES != 2 || NSUB == 4 || (NSUB == 2 && kP1 == 0 && kP2 == 0),
-                "two sub-steps: all loads in sub-steps 1 and 0");
-  auto issue_load = [&](uint8_t* st, int j, int L) {
-    if (L < Cfg::kScaleLoads) {
-      issue_group_load((j + 3) / 4, (j + 3) % 4, L);
-    } else {
-      const int q = L - Cfg::kScaleLoads, i = q >> 1;
-      const uint32_t dst = lds_addr(st + 1024 * (i * WAVES + wave)) + ((q & 1) ? Cfg::kTile : 0);
-      dma_b128((q & 1) ? rb : ra, dst, voff[i], min(j, nk - 1) * Cfg::kRow);
-    }
-  };
-  // the same MFMAs with loads FIRST .. FIRST+CNT-1 of bundle j (into stage st) issued after
-  // every second MFMA
-  auto mma_mix = [&](const Frag (&fa)[FA], const Frag (&fb)[FB], const uint32_t (&sa)[FA][SW],
-                     const uint32_t (&sb)[FB][SW], auto sub, uint8_t* st, int j, auto first,
-                     auto count) {
-    constexpr int SUB = decltype(sub)::value;
-    constexpr int OP = 2 * (SUB % 2), W = SUB / 2;
-    constexpr int FIRST = decltype(first)::value, CNT = decltype(count)::value;
-    static_for<FA * FB>([&](auto nn) {
-      constexpr int n = decltype(nn)::value, i = n / FB, jj = n % FB;
-      acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-          as_operand(fb[jj]), as_operand(fa[i]), acc[i][jj], BF, AF, OP, sb[jj][W], OP, sa[i][W]);
-      if constexpr (n % kPer == kPer - 1 && n / kPer < CNT) {
-        issue_load(st, j, FIRST + n / kPer);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    });
-  };
-
-  if constexpr (Cfg::kGroupScales) {
-    issue_group_part(0, 0);
-    issue_group_part(0, 1);
-    issue_group_part(0, 2);
-  }
-  if constexpr (STAGES == 2) {
-    static_for<LOADS>([&](auto L) { issue_load(stage_ptr(0), 0, decltype(L)::value); });
-    static_for<kP3>([&](auto L) { issue_load(stage_ptr(1), 1, decltype(L)::value); });
-    wait_vmcnt<kP3>();
-  } else {
-#pragma unroll
-    for (int s = 0; s < STAGES; ++s) issue_bundle(stage_ptr(s), s);
-    wait_vmcnt<(STAGES - 1) * LOADS>();
-  }
-  __builtin_amdgcn_s_barrier();
-  sread(stage_ptr(0), 0, saC, sbC);
-  lread(stage_ptr(0), 0, fa0, fb0);
-
-  // Step ks on stage cur: sub-steps 0 .. BKS-1, fragments read one sub-step ahead (ping-pong
-  // fa0/fb0, fa1/fb1). Before the MFMAs of the last sub-step: wait until step ks+1 has landed
-  // (own loads; the barrier covers the other waves; steps ks+2 .. ks+STAGES-1 may still be in
-  // flight); every wave then holds all of stage ks in registers, so the stage is refilled at
-  // once with step ks+STAGES; the scales and first sub-step of ks+1 are read meanwhile.
-  auto body = [&](int ks, uint8_t* cur, const uint8_t* nxt) {
-    static_for<NSUB>([&](auto sub) {
-      constexpr int S = decltype(sub)::value;
-      if constexpr (S + 1 < NSUB) {
-        if constexpr (S % 2 == 0) lread(cur, S + 1, fa1, fb1);
-        else lread(cur, S + 1, fa0, fb0);
-      } else {
-        __builtin_amdgcn_sched_barrier(0);
-        wait_vmcnt<(STAGES - 2) * LOADS>();
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage ks are done
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        issue_bundle(cur, ks + STAGES);
-        sread(nxt, ks + 1, saN, sbN);
-        lread(nxt, 0, fa0, fb0);  // the last sub-step (odd) uses fa1/fb1
-      }
-      if constexpr (S % 2 == 0) mma(fa0, fb0, saC, sbC, sub);
-      else mma(fa1, fb1, saC, sbC, sub);
-      __builtin_amdgcn_sched_barrier(0);  // keep one sub-step of fragments live at a time
-    });
-#pragma unroll
-    for (int i = 0; i < FA; ++i)
-#pragma unroll
-      for (int w = 0; w < SW; ++w) saC[i][w] = saN[i][w];
-#pragma unroll
-    for (int j = 0; j < FB; ++j)
-#pragma unroll
-      for (int w = 0; w < SW; ++w) sbC[j][w] = sbN[j][w];
-  };
-  // Two-stage step ks on stage cur with the spread schedule: sub-steps 0 .. 2 carry the rest of
-  // bundle ks+1 (into nxt), the last sub-step starts bundle ks+2 (into cur) after the barrier.
-  auto body2 = [&](int ks, uint8_t* cur, uint8_t* nxt) {
-    static_for<NSUB>([&](auto sub) {
-      constexpr int S = decltype(sub)::value;
-      if constexpr (S + 1 < NSUB) {
-        constexpr int first = S == 0 ? kP3 : S == 1 ? kP3 + kP0 : kP3 + kP0 + kP1;
-        constexpr int cnt = S == 0 ? kP0 : S == 1 ? kP1 : kP2;
-        if constexpr (S % 2 == 0) {
-          lread(cur, S + 1, fa1, fb1);
-          mma_mix(fa0, fb0, saC, sbC, sub, nxt, ks + 1, std::integral_constant<int, first>{},
-                  std::integral_constant<int, cnt>{});
-        } else {
-          lread(cur, S + 1, fa0, fb0);
-          mma_mix(fa1, fb1, saC, sbC, sub, nxt, ks + 1, std::integral_constant<int, first>{},
-                  std::integral_constant<int, cnt>{});
-        }
-      } else {
-        static_assert(NSUB % 2 == 0, "last sub-step uses fa1/fb1");
-        __builtin_amdgcn_sched_barrier(0);
-        wait_vmcnt<0>();
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage ks are done
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        sread(nxt, ks + 1, saN, sbN);
-        lread(nxt, 0, fa0, fb0);
-        mma_mix(fa1, fb1, saC, sbC, sub, cur, ks + 2, std::integral_constant<int, 0>{},
-                std::integral_constant<int, kP3>{});
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    });
-#pragma unroll
-    for (int i = 0; i < FA; ++i)
-#pragma unroll
-      for (int w = 0; w < SW; ++w) saC[i][w] = saN[i][w];
-#pragma unroll
-    for (int j = 0; j < FB; ++j)
-#pragma unroll
-      for (int w = 0; w < SW; ++w) sbC[j][w] = sbN[j][w];
-  };
-  int ks = 0;
-  if constexpr (STAGES == 4) {
-#pragma unroll 1
-    for (; ks + 4 <= nk; ks += 4) {
-      body(ks, stage_ptr(0), stage_ptr(1));
-      body(ks + 1, stage_ptr(1), stage_ptr(2));
-      body(ks + 2, stage_ptr(2), stage_ptr(3));
-      body(ks + 3, stage_ptr(3), stage_ptr(0));
-    }
-    if (ks < nk) body(ks, stage_ptr(0), stage_ptr(1));
-    if (ks + 1 < nk) body(ks + 1, stage_ptr(1), stage_ptr(2));
-    if (ks + 2 < nk) body(ks + 2, stage_ptr(2), stage_ptr(3));
-  } else {
-    // one step per iteration with computed stage pointers: unrolling two steps here doubles
-    // the live fragment registers and spills
-#pragma unroll 1
-    for (; ks < nk; ++ks) body2(ks, stage_ptr(ks & 1), stage_ptr((ks + 1) & 1));
-  }
-  wait_vmcnt<0>();  // no load may still be writing LDS when the workgroup ends
-
-  // Epilogue: acc[i][j][r] = C[m][n], m = wm*32FA + 32 i + (lane % 32),
-  //                                   n = wn*32FB + 32 j + 8 (r / 4) + 4 (lane / 32) + r % 4.
-  // A store straight from that layout writes 16 or 32 bytes into each of 32 rows, and the L2
-  // write-request rate then bounds the kernel's tail. The tile goes through LDS instead (free
-  // now: every wave has passed its last stage read): each wave writes its sub-tile row-major,
-  // then each store instruction writes whole rows (512 or 1024 contiguous bytes). bf16 results
-  // use the hardware round-to-nearest-even pair conversion, which equals rounding the fp32 bit
-  // pattern for every non-NaN input. Rows are padded by 16 bytes so that the 32 rows a write
-  // instruction touches spread over all banks.
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  if constexpr (QOUT) {
-    // Quantized output [P1 paragraph 1: rotate, scale, round and pack the output tile before
-    // it is stored]: the fp32 tile (times 2^alpha) goes to LDS in two halves of 128 rows;
-    // then every quad of lanes takes one 32-column block of a row, as the row quantizer does.
-    constexpr int kPitch = kBN * 4 + 16;
-    constexpr int kPassRows = kBM / 2;
-    static_assert(kPassRows * kPitch <= Cfg::kLds, "fp32 half tile fits in LDS");
-    const int q = t & 3;
-    const int mode = (qo.hadamard ? 1 : 0) | (qo.sr ? 2 : 0) | (qo.ceil ? 4 : 0);
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      if ((wm * 32 * FA) / kPassRows == p) {
-#pragma unroll
-        for (int i = 0; i < FA; ++i)
-#pragma unroll
-          for (int j = 0; j < FB; ++j)
-#pragma unroll
-            for (int rq = 0; rq < 4; ++rq) {
-              const int r = wm * 32 * FA + 32 * i + frow - p * kPassRows;
-              const int c = wn * 32 * FB + 32 * j + 8 * rq + 4 * fhalf;
-              *reinterpret_cast<f32x4*>(smem + r * kPitch + 4 * c) =
-                  f32x4{acc[i][j][4 * rq + 0] * alpha_f, acc[i][j][4 * rq + 1] * alpha_f,
-                        acc[i][j][4 * rq + 2] * alpha_f, acc[i][j][4 * rq + 3] * alpha_f};
-            }
-      }
-      __builtin_amdgcn_s_waitcnt(0xC07F);
-      __builtin_amdgcn_s_barrier();
-      // round rnd: block b = 64 rnd + t / 4 of the half (row b / 8, 32-column block b % 8)
-      constexpr int kRounds = kPassRows * (kBN / 32) / (64 * WAVES / 4);
-#pragma unroll 1
-      for (int rnd = 0; rnd < kRounds; ++rnd) {
-        const int b = rnd * (16 * WAVES) + (t >> 2);
-        const int r = b >> 3, bc = b & 7;
-        const int64_t m = m0 + p * kPassRows + r, nb = n0 + 32 * bc;
-        if (m >= M || nb >= N) continue;  // whole quads leave together
-        const f32x4 lo = *reinterpret_cast<const f32x4*>(smem + r * kPitch + 4 * (32 * bc + 8 * q));
-        const f32x4 hi = *reinterpret_cast<const f32x4*>(smem + r * kPitch + 4 * (32 * bc + 8 * q) + 16);
-        float w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-        const int64_t e0 = m * N + nb + 8 * q;  // row-major index of value 0 in C
-        const uint64_t g = (uint64_t)e0 >> 3;
-        uint32_t sb = 0, word = 0;
-        switch (mode) {
-          case 0: word = mxd::quant_chunk8<false, false, false>(w, q, qo.sign_mask, qo.seed, g, sb); break;
-          case 1: word = mxd::quant_chunk8<true, false, false>(w, q, qo.sign_mask, qo.seed, g, sb); break;
-          case 2: word = mxd::quant_chunk8<false, true, false>(w, q, qo.sign_mask, qo.seed, g, sb); break;
-          case 3: word = mxd::quant_chunk8<true, true, false>(w, q, qo.sign_mask, qo.seed, g, sb); break;
-          case 4: word = mxd::quant_chunk8<false, false, true>(w, q, qo.sign_mask, qo.seed, g, sb); break;
-          case 5: word = mxd::quant_chunk8<true, false, true>(w, q, qo.sign_mask, qo.seed, g, sb); break;
-          case 6: word = mxd::quant_chunk8<false, true, true>(w, q, qo.sign_mask, qo.seed, g, sb); break;
-          default: word = mxd::quant_chunk8<true, true, true>(w, q, qo.sign_mask, qo.seed, g, sb); break;
-        }
-        *reinterpret_cast<uint32_t*>(qo.codes + e0 / 2) = word;
-        if (q == 0) qo.scales[m * (N / 32) + nb / 32] = (uint8_t)sb;
-      }
-      if (p == 0) {
-        __builtin_amdgcn_s_waitcnt(0xC07F);
-        __builtin_amdgcn_s_barrier();
-      }
-    }
-    return;
-  }
-  const bool full = m0 + kBM <= M && n0 + kBN <= N;
-  if (out_bf16) {
-    constexpr int kPitch = kBN * 2 + 16;
-    static_assert(kBM * kPitch <= Cfg::kLds, "bf16 tile fits in LDS");
+    v16f acc[FA][FB];
 #pragma unroll
     for (int i = 0; i < FA; ++i)
 #pragma unroll
       for (int j = 0; j < FB; ++j)
 #pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          const int r = wm * 32 * FA + 32 * i + frow;
-          const int c = wn * 32 * FB + 32 * j + 8 * rq + 4 * fhalf;
-          f32x2 lo = {acc[i][j][4 * rq + 0] * alpha_f, acc[i][j][4 * rq + 1] * alpha_f};
-          f32x2 hi = {acc[i][j][4 * rq + 2] * alpha_f, acc[i][j][4 * rq + 3] * alpha_f};
-          uint2 w;
-          w.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
-          w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2));
-          *reinterpret_cast<uint2*>(smem + r * kPitch + 2 * c) = w;
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    // MFMAs of sub-step SUB: scale word SUB / 2, byte pair selected by op_sel 2 * (SUB % 2)
+    auto mma = [&](const Frag (&fa)[FA], const Frag (&fb)[FB], const uint32_t (&sa)[FA][SW],
+                   const uint32_t (&sb)[FB][SW], auto sub) {
+      constexpr int SUB = decltype(sub)::value;
+      constexpr int OP = 2 * (SUB % 2), W = SUB / 2;
+#pragma unroll
+      for (int i = 0; i < FA; ++i)
+#pragma unroll
+        for (int j = 0; j < FB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              as_operand(fb[j]), as_operand(fa[i]), acc[i][j], BF, AF, OP, sb[j][W], OP, sa[i][W]);
+    };
+
+    Frag fa0[FA], fb0[FB], fa1[FA], fb1[FB];
+    uint32_t saC[FA][SW], sbC[FB][SW], saN[FA][SW], sbN[FB][SW];
+
+    // Every step issues exactly LOADS loads per wave (steps past the end re-read step nk-1 into
+    // a stage nobody reads again), so each wait is a constant count and the loop has no branches.
+    auto issue_step = [&](uint8_t* st, int ks) { issue(st, min(ks, nk - 1)); };
+
+    // Group mode schedule: the load bundle of step j (its code loads, issued two steps ahead)
+    // also carries quarter (j + 3) % 4 of scale group (j + 3) / 4, so group G arrives with the
+    // bundles of steps 4G-3 .. 4G. That makes it complete (loads retire in order) when the
+    // scales of step 4G are first read, at the barrier of step 4G-1, and its first quarter is
+    // requested only after the barrier of step 4G-5, after which nobody reads the previous
+    // occupant of its buffer (group G-2) any more. Quarters 0-2 of group 0 go out on their own.
+    auto issue_bundle = [&](uint8_t* st, int j) {
+      issue_step(st, j);
+      if constexpr (Cfg::kGroupScales) issue_group_part((j + 3) / 4, (j + 3) % 4);
+    };
+    // Spread schedule (2 stages): load L of bundle j (L < S: load L of its scale quarter, S the
+    // number of scale loads per step; L = S + q: code load q / 2 of operand q % 2) is issued
+    // between MFMAs instead of in one burst after the
+    // barrier, so that a full address queue stalls a single load rather than the whole sub-step.
+    // Loads 0 .. kP3-1 go out during the last sub-step of step j-2 (right after its barrier),
+    // the rest during sub-steps 0 .. 2 of step j-1; all of them land by the barrier of step j-1.
+    // FP4: at most one load per pair of MFMAs; FP8 (MFMAs twice as long): one per MFMA
+    constexpr int kPer = F8 ? 1 : 2;
+    constexpr int kP3 = SPLIT3, kP0 = SPLIT0, kP1 = SPLIT1, kP2 = LOADS - kP3 - kP0 - kP1;
+    static_assert(STAGES != 2 || (kP2 >= 0 && kPer * kP3 <= FA * FB && kPer * kP0 <= FA * FB &&
+                  kPer * kP1 <= FA * FB && kPer * kP2 <= FA * FB), "loads per sub-step");
+    static_assert(STAGES != 2 || NSUB == 4 || (NSUB == 2 && kP1 == 0 && kP2 == 0),
+                  "two sub-steps: all loads in sub-steps 1 and 0");
+    auto issue_load = [&](uint8_t* st, int j, int L) {
+      if (L < Cfg::kScaleLoads) {
+        issue_group_load((j + 3) / 4, (j + 3) % 4, L);
+      } else {
+        const int q = L - Cfg::kScaleLoads, i = q >> 1;
+        const uint32_t dst = lds_addr(st + 1024 * (i * WAVES + wave)) + ((q & 1) ? Cfg::kTile : 0);
+        dma_b128((q & 1) ? rb : ra, dst, voff[i], min(j, nk - 1) * Cfg::kRow);
+      }
+    };
+    // the same MFMAs with loads FIRST .. FIRST+CNT-1 of bundle j (into stage st) issued after
+    // every second MFMA
+    auto mma_mix = [&](const Frag (&fa)[FA], const Frag (&fb)[FB], const uint32_t (&sa)[FA][SW],
+                       const uint32_t (&sb)[FB][SW], auto sub, uint8_t* st, int j, auto first,
+                       auto count) {
+      constexpr int SUB = decltype(sub)::value;
+      constexpr int OP = 2 * (SUB % 2), W = SUB / 2;
+      constexpr int FIRST = decltype(first)::value, CNT = decltype(count)::value;
+      static_for<FA * FB>([&](auto nn) {
+        constexpr int n = decltype(nn)::value, i = n / FB, jj = n % FB;
+        acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            as_operand(fb[jj]), as_operand(fa[i]), acc[i][jj], BF, AF, OP, sb[jj][W], OP, sa[i][W]);
+        if constexpr (n % kPer == kPer - 1 && n / kPer < CNT) {
+          issue_load(st, j, FIRST + n / kPer);
+          __builtin_amdgcn_sched_barrier(0);
         }
-    __builtin_amdgcn_s_waitcnt(0xC07F);
+      });
+    };
+
+    if constexpr (Cfg::kGroupScales) {
+      issue_group_part(0, 0);
+      issue_group_part(0, 1);
+      issue_group_part(0, 2);
+    }
+    if constexpr (STAGES == 2) {
+      static_for<LOADS>([&](auto L) { issue_load(stage_ptr(0), 0, decltype(L)::value); });
+      static_for<kP3>([&](auto L) { issue_load(stage_ptr(1), 1, decltype(L)::value); });
+      wait_vmcnt<kP3>();
+    } else {
+#pragma unroll
+      for (int s = 0; s < STAGES; ++s) issue_bundle(stage_ptr(s), s);
+      wait_vmcnt<(STAGES - 1) * LOADS>();
+    }
     __builtin_amdgcn_s_barrier();
-    // instruction q of wave w: rows 2 (q WAVES + w) + lane / 32, 16-byte chunk lane % 32
-    constexpr int kReads = kBM / 2 / WAVES;
-#pragma unroll 8
-    for (int q = 0; q < kReads; ++q) {
-      const int r = 2 * (q * WAVES + wave) + fhalf;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(smem + r * kPitch + 16 * frow);
-      const int64_t m = m0 + r, n = n0 + 8 * frow;
-      // non-temporal: the output streams past L2 instead of displacing the operand panels the
-      // XCD's other tiles are still reading there
-      if (full || (m < M && n < N))
-        __builtin_nontemporal_store(
-            v, reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(C) + m * ldc + n));
-    }
-  } else {
-    // fp32: two passes of 128 rows (the waves with wm == p fill pass p)
-    constexpr int kPitch = kBN * 4 + 16;
-    constexpr int kPassRows = kBM / 2;
-    static_assert(kPassRows * kPitch <= Cfg::kLds, "fp32 half tile fits in LDS");
+    sread(stage_ptr(0), 0, saC, sbC);
+    lread(stage_ptr(0), 0, fa0, fb0);
+
+    // Step ks on stage cur: sub-steps 0 .. BKS-1, fragments read one sub-step ahead (ping-pong
+    // fa0/fb0, fa1/fb1). Before the MFMAs of the last sub-step: wait until step ks+1 has landed
+    // (own loads; the barrier covers the other waves; steps ks+2 .. ks+STAGES-1 may still be in
+    // flight); every wave then holds all of stage ks in registers, so the stage is refilled at
+    // once with step ks+STAGES; the scales and first sub-step of ks+1 are read meanwhile.
+    auto body = [&](int ks, uint8_t* cur, const uint8_t* nxt) {
+      static_for<NSUB>([&](auto sub) {
+        constexpr int S = decltype(sub)::value;
+        if constexpr (S + 1 < NSUB) {
+          if constexpr (S % 2 == 0) lread(cur, S + 1, fa1, fb1);
+          else lread(cur, S + 1, fa0, fb0);
+        } else {
+          __builtin_amdgcn_sched_barrier(0);
+          wait_vmcnt<(STAGES - 2) * LOADS>();
+          __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage ks are done
+          __builtin_amdgcn_s_barrier();
+          __builtin_amdgcn_sched_barrier(0);
+          issue_bundle(cur, ks + STAGES);
+          sread(nxt, ks + 1, saN, sbN);
+          lread(nxt, 0, fa0, fb0);  // the last sub-step (odd) uses fa1/fb1
+        }
+        if constexpr (S % 2 == 0) mma(fa0, fb0, saC, sbC, sub);
+        else mma(fa1, fb1, saC, sbC, sub);
+        __builtin_amdgcn_sched_barrier(0);  // keep one sub-step of fragments live at a time
+      });
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      if ((wm * 32 * FA) / kPassRows == p) {
+      for (int i = 0; i < FA; ++i)
+#pragma unroll
+        for (int w = 0; w < SW; ++w) saC[i][w] = saN[i][w];
+#pragma unroll
+      for (int j = 0; j < FB; ++j)
+#pragma unroll
+        for (int w = 0; w < SW; ++w) sbC[j][w] = sbN[j][w];
+    };
+    // Two-stage step ks on stage cur with the spread schedule: sub-steps 0 .. 2 carry the rest of
+    // bundle ks+1 (into nxt), the last sub-step starts bundle ks+2 (into cur) after the barrier.
+    auto body2 = [&](int ks, uint8_t* cur, uint8_t* nxt) {
+      static_for<NSUB>([&](auto sub) {
+        constexpr int S = decltype(sub)::value;
+        if constexpr (S + 1 < NSUB) {
+          constexpr int first = S == 0 ? kP3 : S == 1 ? kP3 + kP0 : kP3 + kP0 + kP1;
+          constexpr int cnt = S == 0 ? kP0 : S == 1 ? kP1 : kP2;
+          if constexpr (S % 2 == 0) {
+            lread(cur, S + 1, fa1, fb1);
+            mma_mix(fa0, fb0, saC, sbC, sub, nxt, ks + 1, std::integral_constant<int, first>{},
+                    std::integral_constant<int, cnt>{});
+          } else {
+            lread(cur, S + 1, fa0, fb0);
+            mma_mix(fa1, fb1, saC, sbC, sub, nxt, ks + 1, std::integral_constant<int, first>{},
+                    std::integral_constant<int, cnt>{});
+          }
+        } else {
+          static_assert(NSUB % 2 == 0, "last sub-step uses fa1/fb1");
+          __builtin_amdgcn_sched_barrier(0);
+          wait_vmcnt<0>();
+          __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage ks are done
+          __builtin_amdgcn_s_barrier();
+          __builtin_amdgcn_sched_barrier(0);
+          sread(nxt, ks + 1, saN, sbN);
+          lread(nxt, 0, fa0, fb0);
+          mma_mix(fa1, fb1, saC, sbC, sub, cur, ks + 2, std::integral_constant<int, 0>{},
+                  std::integral_constant<int, kP3>{});
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+#pragma unroll
+      for (int i = 0; i < FA; ++i)
+#pragma unroll
+        for (int w = 0; w < SW; ++w) saC[i][w] = saN[i][w];
+#pragma unroll
+      for (int j = 0; j < FB; ++j)
+#pragma unroll
+        for (int w = 0; w < SW; ++w) sbC[j][w] = sbN[j][w];
+    };
+    int ks = 0;
+    if constexpr (STAGES == 4) {
+#pragma unroll 1
+      for (; ks + 4 <= nk; ks += 4) {
+        body(ks, stage_ptr(0), stage_ptr(1));
+        body(ks + 1, stage_ptr(1), stage_ptr(2));
+        body(ks + 2, stage_ptr(2), stage_ptr(3));
+        body(ks + 3, stage_ptr(3), stage_ptr(0));
+      }
+      if (ks < nk) body(ks, stage_ptr(0), stage_ptr(1));
+      if (ks + 1 < nk) body(ks + 1, stage_ptr(1), stage_ptr(2));
+      if (ks + 2 < nk) body(ks + 2, stage_ptr(2), stage_ptr(3));
+    } else {
+      // one step per iteration with computed stage pointers: unrolling two steps here doubles
+      // the live fragment registers and spills
+#pragma unroll 1
+      for (; ks < nk; ++ks) body2(ks, stage_ptr(ks & 1), stage_ptr((ks + 1) & 1));
+    }
+    wait_vmcnt<0>();  // no load may still be writing LDS when the workgroup ends
+
+    // Epilogue: acc[i][j][r] = C[m][n], m = wm*32FA + 32 i + (lane % 32),
+    //                                   n = wn*32FB + 32 j + 8 (r / 4) + 4 (lane / 32) + r % 4.
+    // A store straight from that layout writes 16 or 32 bytes into each of 32 rows, and the L2
+    // write-request rate then bounds the kernel's tail. The tile goes through LDS instead (free
+    // now: every wave has passed its last stage read): each wave writes its sub-tile row-major,
+    // then each store instruction writes whole rows (512 or 1024 contiguous bytes). bf16 results
+    // use the hardware round-to-nearest-even pair conversion, which equals rounding the fp32 bit
+    // pattern for every non-NaN input. Rows are padded by 16 bytes so that the 32 rows a write
+    // instruction touches spread over all banks.
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    if constexpr (QOUT) {
+      // Quantized output [P1 paragraph 1: rotate, scale, round and pack the output tile before
+      // it is stored]: the fp32 tile (times 2^alpha) goes to LDS in two halves of 128 rows;
+      // then every quad of lanes takes one 32-column block of a row, as the row quantizer does.
+      constexpr int kPitch = kBN * 4 + 16;
+      constexpr int kPassRows = kBM / 2;
+      static_assert(kPassRows * kPitch <= Cfg::kLds, "fp32 half tile fits in LDS");
+      const int q = t & 3;
+      const int mode = (qo.hadamard ? 1 : 0) | (qo.sr ? 2 : 0) | (qo.ceil ? 4 : 0);
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        if ((wm * 32 * FA) / kPassRows == p) {
+#pragma unroll
+          for (int i = 0; i < FA; ++i)
+#pragma unroll
+            for (int j = 0; j < FB; ++j)
+#pragma unroll
+              for (int rq = 0; rq < 4; ++rq) {
+                const int r = wm * 32 * FA + 32 * i + frow - p * kPassRows;
+                const int c = wn * 32 * FB + 32 * j + 8 * rq + 4 * fhalf;
+                *reinterpret_cast<f32x4*>(smem + r * kPitch + 4 * c) =
+                    f32x4{acc[i][j][4 * rq + 0] * alpha_f, acc[i][j][4 * rq + 1] * alpha_f,
+                          acc[i][j][4 * rq + 2] * alpha_f, acc[i][j][4 * rq + 3] * alpha_f};
+              }
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_s_barrier();
+        // round rnd: block b = 64 rnd + t / 4 of the half (row b / 8, 32-column block b % 8)
+        constexpr int kRounds = kPassRows * (kBN / 32) / (64 * WAVES / 4);
+#pragma unroll 1
+        for (int rnd = 0; rnd < kRounds; ++rnd) {
+          const int b = rnd * (16 * WAVES) + (t >> 2);
+          const int r = b >> 3, bc = b & 7;
+          const int64_t m = m0 + p * kPassRows + r, nb = n0 + 32 * bc;
+          if (m >= M || nb >= N) continue;  // whole quads leave together
+          const f32x4 lo = *reinterpret_cast<const f32x4*>(smem + r * kPitch + 4 * (32 * bc + 8 * q));
+          const f32x4 hi = *reinterpret_cast<const f32x4*>(smem + r * kPitch + 4 * (32 * bc + 8 * q) + 16);
+          float w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+          const int64_t e0 = m * N + nb + 8 * q;  // row-major index of value 0 in C
+          const uint64_t g = (uint64_t)e0 >> 3;
+          uint32_t sb = 0, word = 0;
+          switch (mode) {
+            case 0: word = mxd::quant_chunk8<false, false, false>(w, q, qo.sign_mask, qo.seed, g, sb); break;
+            case 1: word = mxd::quant_chunk8<true, false, false>(w, q, qo.sign_mask, qo.seed, g, sb); break;
+            case 2: word = mxd::quant_chunk8<false, true, false>(w, q, qo.sign_mask, qo.seed, g, sb); break;
+            case 3: word = mxd::quant_chunk8<true, true, false>(w, q, qo.sign_mask, qo.seed, g, sb); break;
+            case 4: word = mxd::quant_chunk8<false, false, true>(w, q, qo.sign_mask, qo.seed, g, sb); break;
+            case 5: word = mxd::quant_chunk8<true, false, true>(w, q, qo.sign_mask, qo.seed, g, sb); break;
+            case 6: word = mxd::quant_chunk8<false, true, true>(w, q, qo.sign_mask, qo.seed, g, sb); break;
+            default: word = mxd::quant_chunk8<true, true, true>(w, q, qo.sign_mask, qo.seed, g, sb); break;
+          }
+          *reinterpret_cast<uint32_t*>(qo.codes + e0 / 2) = word;
+          if (q == 0) qo.scales[m * (N / 32) + nb / 32] = (uint8_t)sb;
+        }
+        if (p == 0) {
+          __builtin_amdgcn_s_waitcnt(0xC07F);
+          __builtin_amdgcn_s_barrier();
+        }
+      }
+    } else {
+      const bool full = m0 + kBM <= M && n0 + kBN <= N;
+      if (out_bf16) {
+        constexpr int kPitch = kBN * 2 + 16;
+        static_assert(kBM * kPitch <= Cfg::kLds, "bf16 tile fits in LDS");
 #pragma unroll
         for (int i = 0; i < FA; ++i)
 #pragma unroll
           for (int j = 0; j < FB; ++j)
 #pragma unroll
             for (int rq = 0; rq < 4; ++rq) {
-              const int r = wm * 32 * FA + 32 * i + frow - p * kPassRows;
+              const int r = wm * 32 * FA + 32 * i + frow;
               const int c = wn * 32 * FB + 32 * j + 8 * rq + 4 * fhalf;
-              *reinterpret_cast<f32x4*>(smem + r * kPitch + 4 * c) =
-                  f32x4{acc[i][j][4 * rq + 0] * alpha_f, acc[i][j][4 * rq + 1] * alpha_f,
-                        acc[i][j][4 * rq + 2] * alpha_f, acc[i][j][4 * rq + 3] * alpha_f};
+              f32x2 lo = {acc[i][j][4 * rq + 0] * alpha_f, acc[i][j][4 * rq + 1] * alpha_f};
+              f32x2 hi = {acc[i][j][4 * rq + 2] * alpha_f, acc[i][j][4 * rq + 3] * alpha_f};
+              uint2 w;
+              w.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
+              w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2));
+              *reinterpret_cast<uint2*>(smem + r * kPitch + 2 * c) = w;
             }
-      }
-      __builtin_amdgcn_s_waitcnt(0xC07F);
-      __builtin_amdgcn_s_barrier();
-      // instruction q of wave w: row q WAVES + w, 16-byte chunk lane
-      constexpr int kReads = kPassRows / WAVES;
-#pragma unroll 8
-      for (int q = 0; q < kReads; ++q) {
-        const int r = q * WAVES + wave;
-        const f32x4 v = *reinterpret_cast<const f32x4*>(smem + r * kPitch + 16 * lane);
-        const int64_t m = m0 + p * kPassRows + r, n = n0 + 4 * lane;
-        if (full || (m < M && n < N))
-          __builtin_nontemporal_store(
-              v, reinterpret_cast<f32x4*>(reinterpret_cast<float*>(C) + m * ldc + n));
-      }
-      if (p == 0) {
         __builtin_amdgcn_s_waitcnt(0xC07F);
         __builtin_amdgcn_s_barrier();
+        // instruction q of wave w: rows 2 (q WAVES + w) + lane / 32, 16-byte chunk lane % 32
+        constexpr int kReads = kBM / 2 / WAVES;
+#pragma unroll 8
+        for (int q = 0; q < kReads; ++q) {
+          const int r = 2 * (q * WAVES + wave) + fhalf;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(smem + r * kPitch + 16 * frow);
+          const int64_t m = m0 + r, n = n0 + 8 * frow;
+          // non-temporal: the output streams past L2 instead of displacing the operand panels the
+          // XCD's other tiles are still reading there
+          if (full || (m < M && n < N))
+            __builtin_nontemporal_store(
+                v, reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(C) + m * ldc + n));
+        }
+      } else {
+        // fp32: two passes of 128 rows (the waves with wm == p fill pass p)
+        constexpr int kPitch = kBN * 4 + 16;
+        constexpr int kPassRows = kBM / 2;
+        static_assert(kPassRows * kPitch <= Cfg::kLds, "fp32 half tile fits in LDS");
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          if ((wm * 32 * FA) / kPassRows == p) {
+#pragma unroll
+            for (int i = 0; i < FA; ++i)
+#pragma unroll
+              for (int j = 0; j < FB; ++j)
+#pragma unroll
+                for (int rq = 0; rq < 4; ++rq) {
+                  const int r = wm * 32 * FA + 32 * i + frow - p * kPassRows;
+                  const int c = wn * 32 * FB + 32 * j + 8 * rq + 4 * fhalf;
+                  *reinterpret_cast<f32x4*>(smem + r * kPitch + 4 * c) =
+                      f32x4{acc[i][j][4 * rq + 0] * alpha_f, acc[i][j][4 * rq + 1] * alpha_f,
+                            acc[i][j][4 * rq + 2] * alpha_f, acc[i][j][4 * rq + 3] * alpha_f};
+                }
+          }
+          __builtin_amdgcn_s_waitcnt(0xC07F);
+          __builtin_amdgcn_s_barrier();
+          // instruction q of wave w: row q WAVES + w, 16-byte chunk lane
+          constexpr int kReads = kPassRows / WAVES;
+#pragma unroll 8
+          for (int q = 0; q < kReads; ++q) {
+            const int r = q * WAVES + wave;
+            const f32x4 v = *reinterpret_cast<const f32x4*>(smem + r * kPitch + 16 * lane);
+            const int64_t m = m0 + p * kPassRows + r, n = n0 + 4 * lane;
+            if (full || (m < M && n < N))
+              __builtin_nontemporal_store(
+                  v, reinterpret_cast<f32x4*>(reinterpret_cast<float*>(C) + m * ldc + n));
+          }
+          if (p == 0) {
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            __builtin_amdgcn_s_barrier();
+          }
+        }
       }
     }
+    // every wave is done with the LDS (the epilogue staging) before the next tile loads into it
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
   }
 }
 
 }  // namespace
+
+// Grid of the streaming kernel: one workgroup per CU (a workgroup holds a whole CU's LDS), each
+// walking tiles, when there are more tiles than CUs; the CU count is rounded down to a multiple
+// of 8 (the XCDs). Without the attribute, one workgroup per tile.
+static int stream_grid(int64_t nblocks) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 8)
+    return (int)nblocks;
+  cus -= cus % 8;
+  return (int)min(nblocks, (int64_t)cus);
+}
 
 hipError_t mx_launch_gemm(const GemmArgs& g) {
   const int64_t nbm = (g.M + kBM - 1) / kBM, nbn = (g.N + kBN - 1) / kBN;
@@ -917,18 +939,19 @@ hipError_t mx_launch_gemm(const GemmArgs& g) {
   const float alpha_f = __builtin_bit_cast(float, (uint32_t)(g.alpha + 127) << 23);
   const int lga = g.ga == 64 ? 6 : g.ga == 32 ? 5 : 0, lgb = g.gb == 64 ? 6 : g.gb == 32 ? 5 : 0;
   const dim3 grid((unsigned)(nbm * nbn));
+  const dim3 resident((unsigned)stream_grid(nbm * nbn));
   // loads of a step issued during sub-steps 3, 0, 1 (the rest during sub-step 2): as early as
   // the at-most-one-load-per-MFMA-pair rule allows
   constexpr int kS3 = kStreamWaves == 4 ? 8 : 4, kS0 = kStreamWaves == 4 ? 8 : 4;
   constexpr int kS1 = kStreamWaves == 4 ? 1 : 2;
   if (g.K % 512 == 0 && g.K > 0)
-    hipLaunchKernelGGL((gemm_mx_stream_kernel<kStreamWaves, 4, 2, kS3, kS0, kS1>), grid,
+    hipLaunchKernelGGL((gemm_mx_stream_kernel<kStreamWaves, 4, 2, kS3, kS0, kS1>), resident,
                        dim3(64 * kStreamWaves), 0, (hipStream_t)g.stream, g.a,
                        g.as, lga, g.b, g.bs, lgb, g.M, g.N, g.K, alpha_f, g.out_bf16 ? 1 : 0, g.c,
                        g.ldc, (int)nbm, (int)nbn, GemmQuantOut{});
   else if (g.K % kBK == 0 && g.K > 0)
-    hipLaunchKernelGGL((gemm_mx_stream_kernel<kStreamWaves, 2, 4>), grid, dim3(64 * kStreamWaves), 0,
-                       (hipStream_t)g.stream, g.a,
+    hipLaunchKernelGGL((gemm_mx_stream_kernel<kStreamWaves, 2, 4>), resident, dim3(64 * kStreamWaves),
+                       0, (hipStream_t)g.stream, g.a,
                        g.as, lga, g.b, g.bs, lgb, g.M, g.N, g.K, alpha_f, g.out_bf16 ? 1 : 0, g.c,
                        g.ldc, (int)nbm, (int)nbn, GemmQuantOut{});
   else
@@ -945,15 +968,15 @@ hipError_t mx_launch_gemm_quant(const GemmArgs& g, const GemmQuantOut& q) {
   if (g.K <= 0 || g.K % kBK != 0) return hipErrorInvalidValue;
   const float alpha_f = __builtin_bit_cast(float, (uint32_t)(g.alpha + 127) << 23);
   const int lga = g.ga == 64 ? 6 : g.ga == 32 ? 5 : 0, lgb = g.gb == 64 ? 6 : g.gb == 32 ? 5 : 0;
-  const dim3 grid((unsigned)(nbm * nbn));
+  const dim3 resident((unsigned)stream_grid(nbm * nbn));
   constexpr int kS3 = kStreamWaves == 4 ? 8 : 4, kS0 = kStreamWaves == 4 ? 8 : 4;
   constexpr int kS1 = kStreamWaves == 4 ? 1 : 2;
   if (g.K % 512 == 0)
-    hipLaunchKernelGGL((gemm_mx_stream_kernel<kStreamWaves, 4, 2, kS3, kS0, kS1, true>), grid,
+    hipLaunchKernelGGL((gemm_mx_stream_kernel<kStreamWaves, 4, 2, kS3, kS0, kS1, true>), resident,
                        dim3(64 * kStreamWaves), 0, (hipStream_t)g.stream, g.a, g.as, lga, g.b,
                        g.bs, lgb, g.M, g.N, g.K, alpha_f, 0, nullptr, 0, (int)nbm, (int)nbn, q);
   else
-    hipLaunchKernelGGL((gemm_mx_stream_kernel<kStreamWaves, 2, 4, 0, 0, 0, true>), grid,
+    hipLaunchKernelGGL((gemm_mx_stream_kernel<kStreamWaves, 2, 4, 0, 0, 0, true>), resident,
                        dim3(64 * kStreamWaves), 0, (hipStream_t)g.stream, g.a, g.as, lga, g.b,
                        g.bs, lgb, g.M, g.N, g.K, alpha_f, 0, nullptr, 0, (int)nbm, (int)nbn, q);
   return hipGetLastError();
@@ -976,7 +999,7 @@ hipError_t mx_launch_gemm_fp8(const GemmArgs& g, int afmt, int bfmt) {
   if ((int64_t)kBM * g.K >= (int64_t)1 << 31) return hipErrorInvalidValue;
   if (g.K <= 0 || g.K % 128 != 0) return hipErrorInvalidValue;
   const float alpha_f = __builtin_bit_cast(float, (uint32_t)(g.alpha + 127) << 23);
-  const dim3 grid((unsigned)(nbm * nbn));
+  const dim3 grid((unsigned)stream_grid(nbm * nbn));
   const int b = (afmt ? 2 : 0) | (bfmt ? 1 : 0);
   switch (b) {
     case 0: return launch_gemm_fp8<0, 0>(g, grid, alpha_f, 0, 0, (int)nbm, (int)nbn);
