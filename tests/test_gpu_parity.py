@@ -256,6 +256,26 @@ def test_gemm_hadamard_alpha(mx, orc):
     assert rel < 0.2
 
 
+@pytest.mark.parametrize("M,N,K", [(8096, 4064, 2048), (4352, 4352, 4096)])
+def test_gemm_chained_tiles(mx, orc, M, N, K):
+    """More 256x256 tiles than compute units, so every workgroup of the resident grid walks
+    several tiles, with Hadamard + SR operands, bf16 output and whole 4-step scale groups.
+    Ragged M and N put partial tiles among them, and the columns of the output rows past N
+    must stay untouched."""
+    a = wl.student_t3((M, K), seed=31).to(DEV)
+    b = wl.normal((N, K), 0.02, seed=32).to(DEV)
+    (aq, as_), (bq, bs) = quantize_pair(mx, a, b, rule=1, rnd=1, had=1, mask=wl.sign_mask())
+    big = torch.full((M, N + 32), 7.0, dtype=torch.bfloat16, device=DEV)
+    out = mx.mx_gemm_fprop(aq, as_, 1, bq, bs, 1, out=big[:, :N], out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, M, 11), np.arange(M - 40, M)]))
+    cols = np.arange(N)
+    C, Cabs = orc.gemm(host(aq), host(as_), 1, host(bq), host(bs), 1, M, N, K, 0,
+                       rows=rows, cols=cols)
+    check_gemm(out, C, Cabs, rows=rows, cols=cols)
+    assert torch.all(big[:, N:] == 7.0)
+
+
 def test_gemm_output_leading_dimension(mx, orc):
     M, N, K = 64, 96, 128
     a = wl.student_t3((M, K), seed=21).to(DEV)
