@@ -29,9 +29,9 @@
  *    |v| >= largest saturates; rounding and the random fields as for E2M1.
  *
  * Parity pins: see the tests under tests/ (exhaustive grid/scale checks, SR enumeration,
- * dense Hadamard matrix, transposition invariance). Philox4x32-10 is pinned against an
- * independent library on the GPU host only; on a CPU-only host its third-party parity is
- * unpinned.
+ * dense Hadamard matrix, transposition invariance). Philox4x32-10 is pinned against rocRAND's
+ * header-only engine, built for the host CPU from the ROCm headers; on a host without those
+ * headers that one pin is skipped.
  */
 #include <math.h>
 #include <pthread.h>
