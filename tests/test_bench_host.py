@@ -1,0 +1,135 @@
+"""Host logic of bench.py that feeds the reported roofline (CPU only, no GPU work).
+
+The HBM traffic of a GEMM launch comes from two rocprofv3 counter passes (FETCH_SIZE, then
+WRITE_SIZE, in KiB per dispatch, one row per hardware instance). Each counter is scaled by what
+it reads for a plain 1 GiB device copy in the same run, and the resident-grid GEMM launches are
+told apart by their order in the step (Fprop, Dgrad, Wgrad). These tests feed synthetic counter
+files with known answers through that code.
+"""
+import csv
+import json
+
+import pytest
+
+import bench
+
+T, K, N = 16384, 28672, 8192          # the 70B down-projection: tokens, FFN, hidden
+SHAPES = {"fprop": (T, N, K), "dgrad": (T, K, N), "wgrad": (N, K, T)}  # (M, N, K) per GEMM
+GEMM = "(anonymous namespace)::gemm_mx_stream_kernel<4, 4, 2, 8, 8, 1, false, 4, 4>(args)"
+QOUT = "(anonymous namespace)::gemm_mx_stream_kernel<4, 4, 2, 8, 8, 1, true, 4, 4>(args)"
+FP8 = "(anonymous namespace)::gemm_mx_stream_kernel<4, 4, 2, 16, 2, 0, false, 0, 0>(args)"
+QUANT = "(anonymous namespace)::quant_rows_kernel<true, true, true, true>(args)"
+COPY = "__amd_rocclr_copyBuffer"
+FETCH_KIB = {"fprop": 1_400_000.0, "dgrad": 1_500_000.0, "wgrad": 1_450_000.0}
+
+
+def out_kib(name):
+    M, Nn, _ = SHAPES[name]
+    return 2 * M * Nn / 1024.0      # bf16 output, write factor 1
+
+
+def write_csv(path, counter, rows):
+    """rows: (dispatch id, kernel name, total value); each value is split over 4 instances."""
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name",
+                                          "Counter_Value"])
+        w.writeheader()
+        for d, name, value in rows:
+            for part in (0.1, 0.2, 0.3, 0.4):
+                w.writerow({"Dispatch_Id": d, "Kernel_Name": name, "Counter_Name": counter,
+                            "Counter_Value": value * part})
+            w.writerow({"Dispatch_Id": d, "Kernel_Name": name, "Counter_Name": "OTHER",
+                        "Counter_Value": 1e12})
+
+
+def dispatches(value_of, copy_kib, steps=3, write_scale=None):
+    """A run in dispatch order: per step, a quantizer and the three GEMMs; then the quantizing
+    epilogue and an MXFP8 GEMM (not the plain MXFP4 kernel), then the calibration copy."""
+    rows, d = [], 1
+    for _ in range(steps):
+        rows.append((d, QUANT, 123.0)); d += 1
+        for name in bench.TRAFFIC_ORDER:
+            v = value_of(name)
+            if write_scale and name in write_scale:
+                v *= write_scale[name]
+            rows.append((d, GEMM, v)); d += 1
+    rows += [(d, QOUT, 9e9), (d + 1, FP8, 9e9), (d + 2, COPY, copy_kib), (d + 3, COPY, 10.0)]
+    return rows
+
+
+@pytest.fixture
+def record_path(tmp_path, monkeypatch):
+    p = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(p))
+    return p
+
+
+def make_files(tmp_path, write_scale=None):
+    fetch_csv, wr_csv = tmp_path / "fetch.csv", tmp_path / "write.csv"
+    # the copy reads 1 GiB but FETCH_SIZE reports half of it (factor 2); WRITE_SIZE reports all
+    write_csv(fetch_csv, "FETCH_SIZE", dispatches(lambda n: FETCH_KIB[n], (1 << 30) / 2048.0))
+    write_csv(wr_csv, "WRITE_SIZE", dispatches(out_kib, (1 << 30) / 1024.0, write_scale=write_scale))
+    return str(fetch_csv), str(wr_csv)
+
+
+def test_counter_values_sums_instances_in_dispatch_order(tmp_path):
+    p = tmp_path / "c.csv"
+    write_csv(p, "FETCH_SIZE", [(7, GEMM, 30.0), (2, GEMM, 10.0), (5, COPY, 4.0), (3, GEMM, 20.0)])
+    vals = bench.counter_values(str(p), "FETCH_SIZE")
+    assert vals[GEMM] == pytest.approx([10.0, 20.0, 30.0])
+    assert vals[COPY] == pytest.approx([4.0])
+
+
+def test_write_traffic_record(tmp_path, record_path, monkeypatch):
+    fetch_csv, wr_csv = make_files(tmp_path)
+    monkeypatch.setattr(bench, "sha", lambda path: "0123456789abcdef")
+    bench.write_traffic(fetch_csv, wr_csv, "llama70b_down")
+    rec = json.load(open(record_path))
+    assert rec["gemm_sha"] == "0123456789abcdef"
+    assert rec["fetch_factor"] == pytest.approx(2.0)
+    assert rec["write_factor"] == pytest.approx(1.0)
+    for name, (M, Nn, Kk) in SHAPES.items():
+        # fetch: KiB x 1024 x 2; write: exactly the bf16 output
+        want = FETCH_KIB[name] * 1024 * 2 + 2 * M * Nn
+        assert rec[f"{name}_hbm_bytes_per_launch"] == pytest.approx(want, rel=1e-12)
+        # packed E2M1 codes (K/2 bytes per row) and one scale byte per 32 of both operands,
+        # plus the bf16 output
+        codes = (M * Kk + Nn * Kk) // 2
+        scales = (M * Kk + Nn * Kk) // 32
+        assert rec[f"{name}_algorithmic_bytes_per_launch"] == codes + scales + 2 * M * Nn
+
+
+def test_load_traffic_checks_kernel_hash(tmp_path, record_path, monkeypatch):
+    fetch_csv, wr_csv = make_files(tmp_path)
+    monkeypatch.setattr(bench, "sha", lambda path: "aaaa")
+    bench.write_traffic(fetch_csv, wr_csv, "llama70b_down")
+    key = "wgrad_hbm_bytes_per_launch"
+    assert bench.load_traffic(key, "llama70b_down") == json.load(open(record_path))[key]
+    assert bench.load_traffic(key, "llama8b_up") is None
+    monkeypatch.setattr(bench, "sha", lambda path: "bbbb")  # the kernel changed since
+    assert bench.load_traffic(key, "llama70b_down") is None
+
+
+def test_write_traffic_rejects_a_launch_that_is_not_its_gemm(tmp_path, record_path):
+    # Dgrad writing 20% more than its output means the order-based labels are off
+    fetch_csv, wr_csv = make_files(tmp_path, write_scale={"dgrad": 1.2})
+    with pytest.raises(SystemExit, match="dgrad"):
+        bench.write_traffic(fetch_csv, wr_csv, "llama70b_down")
+    assert not record_path.exists()
+
+
+def test_write_traffic_needs_the_calibration_copy(tmp_path, record_path):
+    fetch_csv, wr_csv = make_files(tmp_path)
+    rows = [r for r in csv.DictReader(open(fetch_csv)) if r["Kernel_Name"] != COPY]
+    with open(fetch_csv, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=list(rows[0].keys()))
+        w.writeheader()
+        w.writerows(rows)
+    with pytest.raises(SystemExit, match="copy"):
+        bench.write_traffic(fetch_csv, wr_csv, "llama70b_down")
+
+
+def test_write_traffic_other_workload(tmp_path, record_path):
+    fetch_csv, wr_csv = make_files(tmp_path)
+    with pytest.raises(SystemExit):
+        bench.write_traffic(fetch_csv, wr_csv, "llama8b_up")
