@@ -50,9 +50,53 @@ def _dtype_code(x: torch.Tensor) -> int:
 
 
 def _src(x: torch.Tensor):
-    if x.dim() != 2 or not x.is_cuda or x.stride(1) != 1:
+    if not isinstance(x, torch.Tensor) or x.dim() != 2 or not x.is_cuda or x.stride(1) != 1:
         raise ValueError("expected a 2-D CUDA tensor with contiguous rows")
     return x.shape[0], x.shape[1], x.stride(0)
+
+
+def _buf(t, name: str, shape, dtypes, device, rows_only: bool = False):
+    """Checks a caller-supplied buffer before its address goes to a kernel: a tensor on `device`
+    with one of `dtypes` and exactly `shape`, contiguous (rows_only: only its rows contiguous,
+    for outputs with a leading dimension). Raises ValueError / TypeError otherwise."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != torch.device(device):
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {tuple(dtypes)}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if rows_only:
+        if t.dim() != 2 or (t.numel() > 0 and (t.stride(1) != 1 or t.stride(0) < shape[1])):
+            raise ValueError(f"{name} must have contiguous rows")
+    elif not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+_U8 = (torch.uint8,)
+
+
+def _codes_out(t, name, shape, device):
+    """A code or scale output: allocated when None, else checked."""
+    if t is None:
+        return torch.empty(shape, dtype=torch.uint8, device=device)
+    return _buf(t, name, shape, _U8, device)
+
+
+def _operand(q, s, g: int, name: str, k_bytes_per_elem: float = 0.5):
+    """A packed GEMM operand (codes [rows][K * bytes per element], scales [rows / g][K / 32])
+    on a CUDA device; returns (rows, K)."""
+    if not isinstance(q, torch.Tensor) or q.dim() != 2 or not q.is_cuda:
+        raise ValueError(f"{name} codes must be a 2-D CUDA tensor")
+    rows = q.shape[0]
+    K = int(round(q.shape[1] / k_bytes_per_elem))
+    _buf(q, f"{name} codes", tuple(q.shape), _U8, q.device)
+    if int(g) not in (1, 32, 64) or rows % int(g):
+        raise ValueError(f"{name} scale granularity {g} does not divide its {rows} rows")
+    _buf(s, f"{name} scales", (rows // int(g), K // 32), _U8, q.device)
+    return rows, K
 
 
 def _opts(scale_rule, round, hadamard, sign_mask, seed) -> mx_quant_opts:
@@ -69,10 +113,8 @@ def mx_quantize(x: torch.Tensor, axis: int = 1, scale_rule: int = MX_SCALE_FLOOR
     rows, cols, ld = _src(x)
     shape_c = (rows, cols // 2) if axis == 1 else (cols, rows // 2)
     shape_s = (rows, cols // 32) if axis == 1 else (cols, rows // 32)
-    if codes is None:
-        codes = torch.empty(shape_c, dtype=torch.uint8, device=x.device)
-    if scales is None:
-        scales = torch.empty(shape_s, dtype=torch.uint8, device=x.device)
+    codes = _codes_out(codes, "codes", shape_c, x.device)
+    scales = _codes_out(scales, "scales", shape_s, x.device)
     o = _opts(scale_rule, round, hadamard, sign_mask, seed)
     check(lib().mx_quantize(_ptr(x), _dtype_code(x), rows, cols, ld, int(axis), ctypes.byref(o),
                             _ptr(codes), _ptr(scales), _stream(stream)), "mx_quantize")
@@ -87,15 +129,13 @@ def mx_quantize_2d(x: torch.Tensor, scale_rule: int = MX_SCALE_CEIL, round: int 
     transposed."""
     rows, cols, ld = _src(x)
     dev = x.device
-    if codes is None:
-        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
-    if scales is None:
-        scales = torch.empty((rows // 32, cols // 32), dtype=torch.uint8, device=dev)
+    codes = _codes_out(codes, "codes", (rows, cols // 2), dev)
+    scales = _codes_out(scales, "scales", (rows // 32, cols // 32), dev)
     if transposed:
-        if codes_t is None:
-            codes_t = torch.empty((cols, rows // 2), dtype=torch.uint8, device=dev)
-        if scales_t is None:
-            scales_t = torch.empty((cols // 32, rows // 32), dtype=torch.uint8, device=dev)
+        codes_t = _codes_out(codes_t, "codes_t", (cols, rows // 2), dev)
+        scales_t = _codes_out(scales_t, "scales_t", (cols // 32, rows // 32), dev)
+    else:
+        codes_t = scales_t = None
     o = _opts(scale_rule, round, 0, 0, seed)
     check(lib().mx_quantize_2d(_ptr(x), _dtype_code(x), rows, cols, ld, ctypes.byref(o),
                                _ptr(codes), _ptr(scales), _ptr(codes_t), _ptr(scales_t),
@@ -106,8 +146,17 @@ def mx_quantize_2d(x: torch.Tensor, scale_rule: int = MX_SCALE_CEIL, round: int 
 def mx_dequantize(codes: torch.Tensor, scales: torch.Tensor, rows: int, cols: int,
                   block_rows: int = 1, inv_hadamard: int = 0, sign_mask: int = 0,
                   out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    if not isinstance(codes, torch.Tensor) or not codes.is_cuda:
+        raise ValueError("codes must be a CUDA tensor")
+    rows, cols, block_rows = int(rows), int(cols), int(block_rows)
+    if block_rows not in (1, 32) or rows % block_rows:
+        raise ValueError("block_rows must be 1 or 32 and divide rows")
+    dev = codes.device
+    _buf(codes, "codes", (rows, cols // 2), _U8, dev)
+    _buf(scales, "scales", (rows // block_rows, cols // 32), _U8, dev)
     if out is None:
-        out = torch.empty((rows, cols), dtype=torch.float32, device=codes.device)
+        out = torch.empty((rows, cols), dtype=torch.float32, device=dev)
+    _buf(out, "out", (rows, cols), (torch.float32,), dev)
     check(lib().mx_dequantize(_ptr(codes), _ptr(scales), rows, cols, int(block_rows),
                               int(inv_hadamard), int(sign_mask) & 0xFFFFFFFF, _ptr(out),
                               _stream(stream)), "mx_dequantize")
@@ -117,17 +166,16 @@ def mx_dequantize(codes: torch.Tensor, scales: torch.Tensor, rows: int, cols: in
 def _out(out, rows, cols, out_dtype, device):
     if out is None:
         out = torch.empty((rows, cols), dtype=out_dtype, device=device)
+    _buf(out, "out", (rows, cols), (torch.bfloat16, torch.float32), device, rows_only=True)
     code = MX_BF16 if out.dtype == torch.bfloat16 else MX_F32
-    if out.dtype not in (torch.bfloat16, torch.float32) or out.stride(1) != 1:
-        raise ValueError("output must be bf16 or fp32 with contiguous rows")
     return out, code
 
 
 def _gemm(name, aq, as_, ga, bq, bs, gb, alpha_exp, out_dtype, out, stream):
-    M, K = aq.shape[0], 2 * aq.shape[1]
-    N = bq.shape[0]
-    if 2 * bq.shape[1] != K:
-        raise ValueError("operands disagree on the reduction length")
+    M, K = _operand(aq, as_, ga, "A")
+    N, Kb = _operand(bq, bs, gb, "B")
+    if Kb != K or bq.device != aq.device:
+        raise ValueError("operands disagree on the reduction length or the device")
     out, code = _out(out, M, N, out_dtype, aq.device)
     check(getattr(lib(), name)(_ptr(aq), _ptr(as_), int(ga), _ptr(bq), _ptr(bs), int(gb), M, N, K,
                                int(alpha_exp), code, _ptr(out), out.stride(0), _stream(stream)),
@@ -158,14 +206,12 @@ def mx_gemm_fprop_quant(xq, xs, gx, wq, ws, gw, alpha_exp=0, scale_rule=MX_SCALE
                         scales=None, stream=None):
     """Y = 2^alpha X W^T in fp32, quantized in the GEMM epilogue along its rows (1x32 blocks
     along N, options as for mx_quantize) -> (codes [T][N/2], scales [T][N/32])."""
-    T, K = xq.shape[0], 2 * xq.shape[1]
-    N = wq.shape[0]
-    if 2 * wq.shape[1] != K:
-        raise ValueError("operands disagree on the reduction length")
-    if codes is None:
-        codes = torch.empty((T, N // 2), dtype=torch.uint8, device=xq.device)
-    if scales is None:
-        scales = torch.empty((T, N // 32), dtype=torch.uint8, device=xq.device)
+    T, K = _operand(xq, xs, gx, "X")
+    N, Kw = _operand(wq, ws, gw, "W")
+    if Kw != K or wq.device != xq.device:
+        raise ValueError("operands disagree on the reduction length or the device")
+    codes = _codes_out(codes, "codes", (T, N // 2), xq.device)
+    scales = _codes_out(scales, "scales", (T, N // 32), xq.device)
     o = _opts(scale_rule, round, hadamard, sign_mask, seed)
     check(lib().mx_gemm_fprop_quant(_ptr(xq), _ptr(xs), int(gx), _ptr(wq), _ptr(ws), int(gw), T, N,
                                     K, int(alpha_exp), ctypes.byref(o), _ptr(codes), _ptr(scales),
@@ -183,10 +229,8 @@ def mx_quantize_mxfp8(x: torch.Tensor, fmt: int = MX_E4M3, axis: int = 1,
     rows, cols, ld = _src(x)
     shape_c = (rows, cols) if axis == 1 else (cols, rows)
     shape_s = (rows, cols // 32) if axis == 1 else (cols, rows // 32)
-    if codes is None:
-        codes = torch.empty(shape_c, dtype=torch.uint8, device=x.device)
-    if scales is None:
-        scales = torch.empty(shape_s, dtype=torch.uint8, device=x.device)
+    codes = _codes_out(codes, "codes", shape_c, x.device)
+    scales = _codes_out(scales, "scales", shape_s, x.device)
     o = _opts(scale_rule, round, hadamard, sign_mask, seed)
     check(lib().mx_quantize_mxfp8(_ptr(x), _dtype_code(x), rows, cols, ld, int(axis), int(fmt),
                                   ctypes.byref(o), _ptr(codes), _ptr(scales), _stream(stream)),
@@ -198,10 +242,10 @@ def mx_gemm_mxfp8(aq, as_, afmt, bq, bs, bfmt, alpha_exp=0, out_dtype=torch.bflo
                   stream=None):
     """C[M][N] = 2^alpha sum_k A[m][k] B[n][k]; aq [M][K], bq [N][K] MXFP8 codes of formats
     afmt / bfmt, scales [M][K/32], [N][K/32]."""
-    M, K = aq.shape
-    N = bq.shape[0]
-    if bq.shape[1] != K:
-        raise ValueError("operands disagree on the reduction length")
+    M, K = _operand(aq, as_, 1, "A", 1.0)
+    N, Kb = _operand(bq, bs, 1, "B", 1.0)
+    if Kb != K or bq.device != aq.device:
+        raise ValueError("operands disagree on the reduction length or the device")
     out, code = _out(out, M, N, out_dtype, aq.device)
     check(lib().mx_gemm_mxfp8(_ptr(aq), _ptr(as_), int(afmt), _ptr(bq), _ptr(bs), int(bfmt), M, N,
                               K, int(alpha_exp), code, _ptr(out), out.stride(0), _stream(stream)),
@@ -222,17 +266,13 @@ def mx_quantize_2d_blocks(x: torch.Tensor, block: int = 32, scale_rule: int = MX
     shape_st = {8: (cols // 8, rows // 8), 32: (cols // 32, rows // 32), 64: (cols // 64, rows // 32)}
     if B not in shape_s:
         raise ValueError("block must be 8, 32 or 64")
-    if codes is None:
-        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
-    if scales is None:
-        scales = torch.empty(shape_s[B], dtype=torch.uint8, device=dev)
+    codes = _codes_out(codes, "codes", (rows, cols // 2), dev)
+    scales = _codes_out(scales, "scales", shape_s[B], dev)
     if not transposed:
         codes_t = scales_t = None
     else:
-        if codes_t is None:
-            codes_t = torch.empty((cols, rows // 2), dtype=torch.uint8, device=dev)
-        if scales_t is None:
-            scales_t = torch.empty(shape_st[B], dtype=torch.uint8, device=dev)
+        codes_t = _codes_out(codes_t, "codes_t", (cols, rows // 2), dev)
+        scales_t = _codes_out(scales_t, "scales_t", shape_st[B], dev)
     o = _opts(scale_rule, round, 0, 0, seed)
     check(lib().mx_quantize_2d_blocks(_ptr(x), _dtype_code(x), rows, cols, ld, B, ctypes.byref(o),
                                       _ptr(codes), _ptr(scales), _ptr(codes_t), _ptr(scales_t),
@@ -247,6 +287,7 @@ def mx_scale_mismatch_map(x: torch.Tensor, scale_rule: int = MX_SCALE_FLOOR, out
     rows, cols, ld = _src(x)
     if out is None:
         out = torch.empty((rows, cols), dtype=torch.int8, device=x.device)
+    _buf(out, "out", (rows, cols), (torch.int8,), x.device)
     check(lib().mx_scale_mismatch_map(_ptr(x), _dtype_code(x), rows, cols, ld, int(scale_rule),
                                       _ptr(out), _stream(stream)), "mx_scale_mismatch_map")
     return out

@@ -916,6 +916,379 @@ void gemm_mx_stream_kernel(const uint8_t* __restrict__ A, const uint8_t* __restr
   }
 }
 
+
+// ---------------------------------------------------------------------------------------------
+// Ping-pong kernel (FP4 operands, K a multiple of 1024). Eight waves, two per SIMD: waves w and
+// w + 4 share a SIMD (the hardware places a workgroup's waves 0-3 on four different SIMDs and
+// waves 4-7 on the same four), and wave w belongs to group g = w / 4. Wave (g, s = w % 4) owns
+// rows 128g .. 128g+127 and columns 64s .. 64s+63 of the 256x256 tile (4 x 2 MFMA tiles, 128
+// fp32 accumulators), so every 64-row block of B is read by one wave of each group and every
+// 128-row half of A by one group only. The two waves of a SIMD take turns: while one
+// issues the 32 MFMAs of a 256-k step from registers (compute phase), the other reads its
+// fragments and scales of its next step from LDS and, in group 0, issues the direct-to-LDS loads
+// of the step after (memory phase). Every phase ends with a workgroup barrier, so the matrix
+// core of a SIMD always has one wave feeding it while the other waits on LDS or memory; a single
+// wave per SIMD would idle the matrix core whenever it waits.
+//
+// Step k lives in LDS stage k % 2 (A then B, 128-byte rows, 16-byte chunk c of row r at position
+// c ^ ((r >> 1) & 7), so 16 consecutive rows read at one chunk hit all 64 banks). Its scales come
+// from scale group k / 4 (buffer (k / 4) % 2: 32 bytes per row = 4 steps of 8 E8M0 bytes; the
+// two 16-byte halves of a row swap places when bit 3 of the row is set, which keeps 16
+// consecutive rows on distinct banks).
+//
+// Which k-blocks one MFMA covers is free as long as both operands agree: sub-step s (0..3) of a
+// step uses k-block 4h + s on lane half h. A lane's fragment of sub-step s is then chunk 4h + s
+// of its row, and its four scale bytes of a step are one aligned word (bytes 4h .. 4h+3 of the
+// row's 8), whose byte s the MFMA selects with op_sel = s.
+//
+// Timeline per tile (n steps; M = memory phase, C = compute phase, | = barrier):
+//   group 0:   M0 | C0 | M1 | C1 | ... | M(n-1) | C(n-1) | (idle)   |
+//   group 1: (idle) | M0 | C0 | M1 | ... | C(n-2) | M(n-1) | C(n-1) |
+// A step's direct loads (64 KiB of codes) take the load path about half a phase; issued by one
+// group in one phase they would outlast the partner's compute phase. So each group loads one
+// operand: group 0's M(k) issues A of step k+1 into stage (k+1) % 2 (whose last reader was
+// group 1's M(k-1)) and one quarter of a scale group, waited for at the end of its C(k); wave s
+// of group 1, once its own M(k) reads of stage k % 2 are complete, issues the 64 B rows it and
+// wave s of group 0 read (group 0's M(k) is a phase older), for step k+2 into that stage, and
+// waits for them at the end of its M(k+1). Steps 0 and 1 and scale group 0 are loaded up front.
+// ---------------------------------------------------------------------------------------------
+namespace pp {
+constexpr int kThreads = 512;
+constexpr int kRow = 128;                    // code bytes per row per step (256 FP4 values)
+constexpr int kTile = 256 * kRow;            // one operand's codes of a step: 32 KiB
+constexpr int kStage = 2 * kTile;            // A then B
+constexpr int kGrpRow = 32;                  // scale bytes per row per group (4 steps)
+constexpr int kGrpOp = 256 * kGrpRow;        // 8 KiB per operand
+constexpr int kGrp = 2 * kGrpOp;             // A then B
+constexpr int kLds = 2 * kStage + 2 * kGrp;  // 160 KiB
+constexpr int kBf16Pitch = 256 * 2 + 16;     // epilogue staging row pitch (bf16)
+constexpr int kF32Pitch = 256 * 4 + 16;      // epilogue staging row pitch (fp32, 128-row passes)
+static_assert(256 * kBf16Pitch <= kLds && 128 * kF32Pitch <= kLds, "staging fits in LDS");
+
+__device__ __forceinline__ void barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// tile index -> first row of A and of B, in the order of the streaming kernel: each XCD gets a
+// contiguous range of tiles, walked in groups of 4 tile rows
+__device__ __forceinline__ void tile_origin(int tile, int nbm, int nbn, int64_t& m0, int64_t& n0) {
+  const int nblocks = nbm * nbn;
+  int bid = tile;
+  const int per_xcd = nblocks / 8;
+  if (bid < per_xcd * 8) bid = (bid % 8) * per_xcd + bid / 8;
+  constexpr int kGroup = 4;
+  const int group = bid / (kGroup * nbn);
+  const int first_m = group * kGroup;
+  const int gsize = min(nbm - first_m, kGroup);
+  const int in_group = bid - group * kGroup * nbn;
+  m0 = (int64_t)(first_m + in_group % gsize) * 256;
+  n0 = (int64_t)(in_group / gsize) * 256;
+}
+
+// buffer descriptors of one tile's operands: 256-row code panels and their scale rows; loads
+// past the operand's last row read zero
+struct TileRes {
+  i32x4 ra, rb, rsa, rsb;
+};
+__device__ __forceinline__ TileRes tile_res(const uint8_t* A, const uint8_t* As, int lga,
+                                            const uint8_t* B, const uint8_t* Bs, int lgb,
+                                            int64_t M, int64_t N, int64_t K, int64_t m0,
+                                            int64_t n0) {
+  const int64_t kbytes = K / 2, nkb = K / 32;
+  const int64_t rows_a = min((int64_t)256, M - m0), rows_b = min((int64_t)256, N - n0);
+  TileRes r;
+  r.ra = rsrc_words(A + m0 * kbytes, rows_a * kbytes);
+  r.rb = rsrc_words(B + n0 * kbytes, rows_b * kbytes);
+  // rows_a and rows_b are multiples of the scale granularity, so the scale rows of rows past
+  // the operand start at or beyond the end of these ranges
+  r.rsa = rsrc_words(As + (m0 >> lga) * nkb, (rows_a >> lga) * nkb);
+  r.rsb = rsrc_words(Bs + (n0 >> lgb) * nkb, (rows_b >> lgb) * nkb);
+  return r;
+}
+}  // namespace pp
+
+__global__ __launch_bounds__(pp::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_mx_pp_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, int lga,
+                       const uint8_t* __restrict__ B, const uint8_t* __restrict__ Bs, int lgb,
+                       int64_t M, int64_t N, int64_t K, float alpha_f, int out_bf16,
+                       void* __restrict__ C, int64_t ldc, int nbm, int nbn) {
+  using namespace pp;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kLds];
+  const int nblocks = nbm * nbn;
+  const int64_t kbytes = K / 2, nkb = K / 32;
+  const int n = (int)(K / 256);  // steps per tile, a multiple of 4
+
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int s = w & 3, g = w >> 2;           // index within the group, and the group
+  const int wm = g, wn = s;
+  const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(smem);
+
+  // Direct-to-LDS loads of wave s of a group (lane-dependent parts; the rest is scalar):
+  //  * A code load q (0..7, group 0) of a step fills 1 KiB block b = s + 4q of the A stage tile:
+  //    rows 8b + lane / 8, position lane % 8, i.e. chunk (lane % 8) ^ ((row >> 1) & 7), whose
+  //    phase depends on the lane only: byte row * kbytes + 16 chunk of the operand panel, with
+  //    32 q * kbytes of it a per-load constant;
+  //  * B code load q (0..7, group 1) fills block b = 8s + q (rows 64s + 8q + lane / 8), whose
+  //    chunk phase (4q + lane / 16) % 8 alternates with the parity of q;
+  //  * scale quarter p (0..3, group 0 only) is load u = 4p + s: operand p / 2, rows
+  //    128 (p % 2) + 32 s + lane / 2, position lane % 2, i.e. half (lane % 2) ^ bit 3 of the
+  //    row = bit 4 of the lane.
+  auto dma_lane_offsets = [&](int lane, int& voff0, int& goff0) {
+    const int row = 8 * s + (lane >> 3);
+    const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+    voff0 = row * (int)kbytes + 16 * chunk;
+    const int half = (lane & 1) ^ ((lane >> 4) & 1);
+    goff0 = 16 * half;  // + the row's scale offset, added per operand below
+  };
+
+  for (int tile = blockIdx.x; tile < nblocks; tile += gridDim.x) {
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));  // per tile: keep lane setup out of the loop-carried state
+    const int lane = t & 63;
+    const int frow = lane & 31, h = lane >> 5;
+    int64_t m0, n0;
+    tile_origin(tile, nbm, nbn, m0, n0);
+    const TileRes R = tile_res(A, As, lga, B, Bs, lgb, M, N, K, m0, n0);
+
+    int voff0, goff_half;
+    dma_lane_offsets(lane, voff0, goff_half);
+    // B loads of group 1: rows 64s + 8q + lane / 8; q even / odd have chunk phases differing in
+    // bit 2
+    const int bchunk = (lane & 7) ^ ((lane >> 4) & 7);
+    const int voffb0 = (64 * s + (lane >> 3)) * (int)kbytes + 16 * bchunk;
+    const int voffb1 = (64 * s + (lane >> 3)) * (int)kbytes + 16 * (bchunk ^ 4);
+    // scale row offset of quarter p's row for lane: (row >> lg) * nkb, row = 128 (p % 2) + 32 w
+    // + lane / 2; the scalar part goes in soffset, the lane part here (zero for g = 32 and 64,
+    // where the lane's row stays inside one scale row)
+    const int goff_a = (lga == 0 ? (lane >> 1) * (int)nkb : 0) + goff_half;
+    const int goff_b = (lgb == 0 ? (lane >> 1) * (int)nkb : 0) + goff_half;
+
+    // Step j's code loads by wave s of group op (0: A, all 256 rows over the group; 1: B rows
+    // 64s .. 64s+63): 8 blocks of 1 KiB into stage j % 2. The row offsets stay in the lane
+    // offset (the buffer range check, which zeroes rows past the operand, applies to it); only
+    // the k offset is scalar.
+    // (The lane offsets pass through an empty asm at each use, so that the eight per-load
+    // offsets are recomputed there instead of being held in registers across the loop.)
+    auto issue_codes = [&](const TileRes& r, int j, int op) {
+      const uint32_t st = lds0 + (j & 1) * kStage;
+      if (op == 0) {
+        int v0 = voff0;
+        asm volatile("" : "+v"(v0));
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          dma_b128(r.ra, st + 1024 * (s + 4 * q), v0 + q * 32 * (int)kbytes, j * kRow);
+      } else {
+        int v0 = voffb0, v1 = voffb1;
+        asm volatile("" : "+v"(v0), "+v"(v1));
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          dma_b128(r.rb, st + kTile + 1024 * (8 * s + q), ((q & 1) ? v1 : v0) + 8 * q * (int)kbytes,
+                   j * kRow);
+      }
+    };
+    auto issue_quarter = [&](const TileRes& r, int G, int p) {
+      const int op = p >> 1;
+      const int row0 = 128 * (p & 1) + 32 * s;  // first row of this wave's piece
+      const int lg = op ? lgb : lga;
+      const uint32_t dst = lds0 + 2 * kStage + (G & 1) * kGrp + op * kGrpOp + 1024 * (4 * (p & 1) + s);
+      int voff = op ? goff_b : goff_a;
+      asm volatile("" : "+v"(voff));
+      voff += (row0 >> lg) * (int)nkb;
+      dma_b128(op ? r.rsb : r.rsa, dst, voff, G * kGrpRow);
+    };
+
+    // Steps 0 and 1 of a tile, scale group 0 and the first quarter of group 1: group 0 loads
+    // A and the scales, group 1 loads B. The first tile of a workgroup issues them here, later
+    // tiles at the end of the previous tile.
+    auto prologue = [&](const TileRes& r) {
+      issue_codes(r, 0, g);
+      if (n > 1) issue_codes(r, 1, g);
+      if (g == 0) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) issue_quarter(r, 0, p);
+        if (4 < n) issue_quarter(r, 1, 0);
+      }
+    };
+    if (tile == (int)blockIdx.x) prologue(R);
+
+    // per-lane LDS offsets of the fragment and scale reads
+    const int phi = (frow >> 1) & 7;
+    const int cb = (4 * h) ^ phi;  // chunk of sub-step s is cb ^ s
+    const uint32_t a_row = (uint32_t)(128 * wm + frow) * kRow;
+    const uint32_t b_row = kTile + (uint32_t)(64 * wn + frow) * kRow;
+    const int sw = (frow >> 3) & 1;
+    const uint32_t sa_row = 2 * kStage + (uint32_t)(128 * wm + frow) * kGrpRow + 4 * h;
+    const uint32_t sb_row = 2 * kStage + kGrpOp + (uint32_t)(64 * wn + frow) * kGrpRow + 4 * h;
+
+    v16f acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    u32x4 fa[4][4], fb[4][2];  // [sub-step][fragment]
+    uint32_t sa[4], sb[2];
+
+    // memory phase of step k: fragments and scale words into registers (plus, in group 0, the
+    // loads of step k + 1); ends with this wave's reads complete
+    auto mem_phase = [&](int k) {
+      const uint8_t* st = smem + (k & 1) * kStage;
+#pragma unroll
+      for (int ss = 0; ss < 4; ++ss) {
+        const uint32_t c = 16u * (uint32_t)(cb ^ ss);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          fa[ss][i] = *reinterpret_cast<const u32x4*>(st + a_row + 4096 * i + c);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          fb[ss][j] = *reinterpret_cast<const u32x4*>(st + b_row + 4096 * j + c);
+      }
+      const int t4 = k & 3;
+      const uint32_t sofs = ((k >> 2) & 1) * kGrp + 16 * ((t4 >> 1) ^ sw) + 8 * (t4 & 1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        sa[i] = *reinterpret_cast<const uint32_t*>(smem + sa_row + 1024 * i + sofs);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        sb[j] = *reinterpret_cast<const uint32_t*>(smem + sb_row + 1024 * j + sofs);
+      if (g == 0 && k >= 1 && k + 1 < n) {
+        issue_codes(R, k + 1, 0);
+        if (k + 4 < n) issue_quarter(R, (k + 4) >> 2, (k + 4) & 3);  // groups of this tile only
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage k are done
+      if (g == 1) {
+        wait_vmcnt<0>();  // B of step k + 1 has landed
+        if (k + 2 < n) issue_codes(R, k + 2, 1);
+      }
+    };
+    auto compute_phase = [&]() {
+      __builtin_amdgcn_s_setprio(1);
+      static_for<4>([&](auto ssc) {
+        constexpr int SS = decltype(ssc)::value;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                as_operand(fb[SS][j]), as_operand(fa[SS][i]), acc[i][j], 4, 4, SS, sb[j], SS, sa[i]);
+      });
+      __builtin_amdgcn_s_setprio(0);
+    };
+
+    wait_vmcnt<0>();  // this tile's steps 0 and 1 and scale group 0
+    barrier();
+    if (g == 0) {
+#pragma unroll 1
+      for (int k = 0; k < n; ++k) {
+        mem_phase(k);
+        barrier();
+        compute_phase();
+        wait_vmcnt<0>();  // A of step k + 1 and the scale quarter have landed
+        barrier();
+      }
+      barrier();  // group 1 computes step n - 1
+    } else {
+      barrier();  // group 0 reads step 0
+#pragma unroll 1
+      for (int k = 0; k < n; ++k) {
+        mem_phase(k);
+        barrier();
+        compute_phase();
+        barrier();
+      }
+    }
+    // both groups are past their last reads of the stages and scale groups: LDS is free
+
+    // Epilogue: acc[i][j][r] = C[m][n], m = 128 wm + 32 i + (lane % 32),
+    //                                   n = 64 wn + 32 j + 8 (r / 4) + 4 (lane / 32) + r % 4.
+    // The tile goes through LDS so that stores write whole rows; the row values are read back
+    // into registers first, so the next tile's first loads can go out before the stores.
+    const int next = tile + (int)gridDim.x;
+    auto prologue_next = [&]() {
+      if (next < nblocks) {
+        int64_t nm0, nn0;
+        tile_origin(next, nbm, nbn, nm0, nn0);
+        prologue(tile_res(A, As, lga, B, Bs, lgb, M, N, K, nm0, nn0));
+      }
+    };
+    const bool full = m0 + 256 <= M && n0 + 256 <= N;
+    if (out_bf16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq) {
+            const int r = 128 * wm + 32 * i + frow;
+            const int c = 64 * wn + 32 * j + 8 * rq + 4 * h;
+            f32x2 lo = {acc[i][j][4 * rq + 0] * alpha_f, acc[i][j][4 * rq + 1] * alpha_f};
+            f32x2 hi = {acc[i][j][4 * rq + 2] * alpha_f, acc[i][j][4 * rq + 3] * alpha_f};
+            uint2 v;
+            v.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
+            v.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2));
+            *reinterpret_cast<uint2*>(smem + r * kBf16Pitch + 2 * c) = v;
+          }
+      barrier();
+      // read q of wave w: row 2 (8 q + w) + lane / 32, 16-byte chunk lane % 32
+      u32x4 v[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        v[q] = *reinterpret_cast<const u32x4*>(smem + (2 * (8 * q + w) + h) * kBf16Pitch + 16 * frow);
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      barrier();
+      prologue_next();
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int64_t m = m0 + 2 * (8 * q + w) + h, nn = n0 + 8 * frow;
+        if (full || (m < M && nn < N))
+          __builtin_nontemporal_store(
+              v[q], reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(C) + m * ldc + nn));
+      }
+    } else {
+      // fp32: two passes of 128 rows (the waves with wm == p fill pass p)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        if (wm == p) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+              for (int rq = 0; rq < 4; ++rq) {
+                const int r = 32 * i + frow;
+                const int c = 64 * wn + 32 * j + 8 * rq + 4 * h;
+                *reinterpret_cast<f32x4*>(smem + r * kF32Pitch + 4 * c) =
+                    f32x4{acc[i][j][4 * rq + 0] * alpha_f, acc[i][j][4 * rq + 1] * alpha_f,
+                          acc[i][j][4 * rq + 2] * alpha_f, acc[i][j][4 * rq + 3] * alpha_f};
+              }
+        }
+        barrier();
+        // read q of wave w: row 8 q + w, 16-byte chunk lane
+        f32x4 v[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+          v[q] = *reinterpret_cast<const f32x4*>(smem + (8 * q + w) * kF32Pitch + 16 * lane);
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        barrier();
+        if (p == 1) prologue_next();
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int64_t m = m0 + 128 * p + 8 * q + w, nn = n0 + 4 * lane;
+          if (full || (m < M && nn < N))
+            __builtin_nontemporal_store(
+                v[q], reinterpret_cast<f32x4*>(reinterpret_cast<float*>(C) + m * ldc + nn));
+        }
+      }
+    }
+  }
+  wait_vmcnt<0>();  // no load may still be writing LDS when the workgroup ends
+}
+
 }  // namespace
 
 // Grid of the streaming kernel: one workgroup per CU (a workgroup holds a whole CU's LDS), each
@@ -944,7 +1317,11 @@ hipError_t mx_launch_gemm(const GemmArgs& g) {
   // the at-most-one-load-per-MFMA-pair rule allows
   constexpr int kS3 = kStreamWaves == 4 ? 8 : 4, kS0 = kStreamWaves == 4 ? 8 : 4;
   constexpr int kS1 = kStreamWaves == 4 ? 1 : 2;
-  if (g.K % 512 == 0 && g.K > 0)
+  if (g.K % 1024 == 0 && g.K > 0)
+    hipLaunchKernelGGL(gemm_mx_pp_kernel, resident, dim3(pp::kThreads), 0, (hipStream_t)g.stream,
+                       g.a, g.as, lga, g.b, g.bs, lgb, g.M, g.N, g.K, alpha_f, g.out_bf16 ? 1 : 0,
+                       g.c, g.ldc, (int)nbm, (int)nbn);
+  else if (g.K % 512 == 0 && g.K > 0)
     hipLaunchKernelGGL((gemm_mx_stream_kernel<kStreamWaves, 4, 2, kS3, kS0, kS1>), resident,
                        dim3(64 * kStreamWaves), 0, (hipStream_t)g.stream, g.a,
                        g.as, lga, g.b, g.bs, lgb, g.M, g.N, g.K, alpha_f, g.out_bf16 ? 1 : 0, g.c,

@@ -69,6 +69,22 @@ class MXLinearConfig:
                  or self.dy_block > 1), (self.wgrad_q, self.dy_block > 1)) if on]
         if any(q.hadamard for q in tiled):
             raise ValueError("tiles are quantized without the Hadamard rotation")
+        # one tile quantization serves two GEMMs: their options must agree on it
+        rule = lambda q: (q.scale_rule, q.round)  # noqa: E731
+        if self.w_block > 1 and self.fprop and self.dgrad and rule(self.fprop_q) != rule(self.dgrad_q):
+            raise ValueError("W tiles are shared by Fprop and Dgrad: fprop_q and dgrad_q must "
+                             "have the same scale_rule and round")
+        if self.dy_block > 1 and self.dgrad and self.wgrad and rule(self.dgrad_q) != rule(self.wgrad_q):
+            raise ValueError("dY tiles are shared by Dgrad and Wgrad: dgrad_q and wgrad_q must "
+                             "have the same scale_rule and round")
+
+    def w_tile_spec(self) -> QuantSpec:
+        """Options of W's tile quantization: Fprop's, or Dgrad's when Fprop is off."""
+        return self.fprop_q if self.fprop else self.dgrad_q
+
+    def dy_tile_spec(self) -> QuantSpec:
+        """Options of dY's tile quantization: Dgrad's, or Wgrad's when Dgrad is off."""
+        return self.dgrad_q if self.dgrad else self.wgrad_q
 
 
 def _q(t: torch.Tensor, axis: int, spec: QuantSpec, seed: int, fp8: int | None = None):
@@ -101,7 +117,7 @@ class MXLinearFunction(torch.autograd.Function):
         ctx.w_tiles = None
         if not cfg.fprop:
             if cfg.dgrad and cfg.w_block > 1:
-                ctx.w_tiles = _tiles(w, cfg.w_block, cfg.fprop_q, sw)
+                ctx.w_tiles = _tiles(w, cfg.w_block, cfg.w_tile_spec(), sw)
             return x @ w.t()
         spec = cfg.fprop_q
         if cfg.fmt == "mxfp8":
@@ -111,7 +127,7 @@ class MXLinearFunction(torch.autograd.Function):
                                  out_dtype=x.dtype)
         xq, xs = _q(x, 1, spec, sx)
         if cfg.w_block > 1:
-            ctx.w_tiles = _tiles(w, cfg.w_block, spec, sw)
+            ctx.w_tiles = _tiles(w, cfg.w_block, cfg.w_tile_spec(), sw)
             wq, ws, gw = ctx.w_tiles[0], ctx.w_tiles[1], cfg.w_block
         else:
             (wq, ws), gw = _q(w, 1, spec, sw), 1
@@ -127,7 +143,7 @@ class MXLinearFunction(torch.autograd.Function):
         dx = dw = None
         dy_tiles = None
         if cfg.dy_block > 1 and not fp8 and (cfg.dgrad or cfg.wgrad):
-            dy_tiles = _tiles(dy, cfg.dy_block, cfg.dgrad_q if cfg.dgrad else cfg.wgrad_q, sdy)
+            dy_tiles = _tiles(dy, cfg.dy_block, cfg.dy_tile_spec(), sdy)
         if ctx.needs_input_grad[0]:
             if cfg.dgrad:
                 spec = cfg.dgrad_q

@@ -210,6 +210,11 @@ GEMM_CASES = [
     (544, 800, 768),     # several tiles in both directions, partial edge tiles
     (256, 256, 2560),    # 256-wide k stages: 10 steps, last scale group partial
     (288, 96, 1536),     # 6 steps, partial M tile
+    # K a multiple of 1024 (the two-waves-per-SIMD kernel): one scale group per 4 steps
+    (32, 32, 1024),      # one partial tile, 4 steps
+    (288, 320, 1024),    # partial tiles in both directions
+    (1056, 96, 2048),    # 5 tile rows, one partial
+    (544, 800, 3072),    # 3 x 4 tiles, 12 steps
 ]
 
 
@@ -227,7 +232,7 @@ def test_gemm_within_bound(mx, orc, M, N, K, out_dtype, which):
     check_gemm(out, C, Cabs)
 
 
-@pytest.mark.parametrize("K", [384, 2048])
+@pytest.mark.parametrize("K", [384, 2048, 3072])
 @pytest.mark.parametrize("ga,gb", [(32, 1), (1, 32), (32, 32)])
 def test_gemm_2d_scales(mx, orc, ga, gb, K):
     M, N = 288, 256
@@ -256,7 +261,7 @@ def test_gemm_hadamard_alpha(mx, orc):
     assert rel < 0.2
 
 
-@pytest.mark.parametrize("M,N,K", [(8096, 4064, 2048), (4352, 4352, 4096)])
+@pytest.mark.parametrize("M,N,K", [(8096, 4064, 2048), (4352, 4352, 4096), (4384, 8224, 1024)])
 def test_gemm_chained_tiles(mx, orc, M, N, K):
     """More 256x256 tiles than compute units, so every workgroup of the resident grid walks
     several tiles, with Hadamard + SR operands, bf16 output and whole 4-step scale groups.
