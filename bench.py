@@ -46,8 +46,10 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="llama70b_down", choices=["llama70b_down", "llama8b_up"])
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-rows", type=int, default=256,
-                   help="source rows per operand quantization in the CPU oracle sample")
+    p.add_argument("--cpu-gemm-rows", type=int, default=64,
+                   help="random full output rows per GEMM in the CPU oracle sample")
+    p.add_argument("--cpu-gemm-elements", type=int, default=1024,
+                   help="random single outputs per GEMM in the CPU oracle sample")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also launch one plain 1 GiB device copy (counter calibration runs)")
     p.add_argument("--step-only", action="store_true",
@@ -111,67 +113,178 @@ class Layer:
         self.mx.mx_quantize(src, axis=axis, scale_rule=rule, round=rnd, hadamard=had,
                             sign_mask=mask, seed=self.seeds[seed_key], codes=c, scales=s)
 
+    # the step's launches in order: (name, kind, source or GEMM operands)
+    QUANTS = (("Xq", "X", 1, "fprop_q"), ("Wq", "W", 1, "fprop_q"), ("dYq", "dY", 1, "dgrad_q"),
+              ("Wt", "W", 0, "dgrad_q"), ("dYt", "dY", 0, "wgrad_q"), ("Xt", "X", 0, "wgrad_q"))
+    GEMMS = (("fprop", "Xq", "Wq", "Y"), ("dgrad", "dYq", "Wt", "dX"), ("wgrad", "dYt", "Xt", "dW"))
+    LAUNCHES = tuple(q[0] for q in QUANTS) + tuple(g[0] for g in GEMMS)
+
     def step(self, ev=None):
+        """One pass of the path. ev: None, or len(LAUNCHES) + 1 events recorded on the current
+        stream around the launches (event i before launch i, the last one after the step)."""
         mx = self.mx
-        if ev is not None:
-            ev["q0"].record()
-        self.quant("Xq", self.X, 1, self.fprop_q, "X")       # largest quantize: X along K
-        if ev is not None:
-            ev["q1"].record()
-        self.quant("Wq", self.W, 1, self.fprop_q, "W")
-        self.quant("dYq", self.dY, 1, self.dgrad_q, "dY")
-        self.quant("Wt", self.W, 0, self.dgrad_q, "W")
-        self.quant("dYt", self.dY, 0, self.wgrad_q, "dY")
-        self.quant("Xt", self.X, 0, self.wgrad_q, "X")
+        i = 0
+        for name, key, axis, q in self.QUANTS:
+            if ev is not None:
+                ev[i].record()
+            i += 1
+            self.quant(name, getattr(self, key), axis, getattr(self, q), key)
         b = self.buf
-        mx.mx_gemm_fprop(*b["Xq"], 1, *b["Wq"], 1, alpha_exp=self.alpha["fprop"], out=self.Y)
-        mx.mx_gemm_dgrad(*b["dYq"], 1, *b["Wt"], 1, alpha_exp=self.alpha["dgrad"], out=self.dX)
+        fns = {"fprop": mx.mx_gemm_fprop, "dgrad": mx.mx_gemm_dgrad, "wgrad": mx.mx_gemm_wgrad}
+        for name, a, bb, o in self.GEMMS:
+            if ev is not None:
+                ev[i].record()
+            i += 1
+            fns[name](*b[a], 1, *b[bb], 1, alpha_exp=self.alpha[name], out=getattr(self, o))
         if ev is not None:
-            ev["w0"].record()
-        mx.mx_gemm_wgrad(*b["dYt"], 1, *b["Xt"], 1, alpha_exp=self.alpha["wgrad"], out=self.dW)
-        if ev is not None:
-            ev["w1"].record()
+            ev[i].record()
+
+    def quant_bytes(self, name):
+        """Algorithmic bytes of one quantize launch: bf16 in, packed codes and scales out."""
+        src = {"Xq": self.X, "Wq": self.W, "dYq": self.dY, "Wt": self.W, "dYt": self.dY,
+               "Xt": self.X}[name]
+        return src.numel() * QUANT_BYTES_PER_ELEM
+
+    def launch_report(self, evs, prefix=""):
+        """Per-launch times averaged over the timed steps' events, with GB/s (quantize) and
+        TFLOP/s (GEMM) and their fractions of the MI355X peaks; plus all six quantize launches
+        together (total bytes over total time)."""
+        n = len(evs)
+        ms = {name: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / n
+              for i, name in enumerate(self.LAUNCHES)}
+        res = {}
+        qb = qt = 0.0
+        for name, *_ in self.QUANTS:
+            gbs = self.quant_bytes(name) / (ms[name] * 1e-3) / 1e9
+            qb += self.quant_bytes(name)
+            qt += ms[name]
+            res[f"{prefix}quant_{name}_ms"] = round(ms[name], 4)
+            res[f"{prefix}quant_{name}_gbs"] = round(gbs, 1)
+            res[f"{prefix}quant_{name}_pct_of_hbm_peak"] = round(100.0 * gbs / PEAK_HBM_GBS, 2)
+        for name, *_ in self.GEMMS:
+            tf = self.flops[name] / (ms[name] * 1e-3) / 1e12
+            res[f"{prefix}{name}_gemm_ms"] = round(ms[name], 4)
+            res[f"{prefix}{name}_gemm_tflops"] = round(tf, 1)
+            res[f"{prefix}{name}_pct_of_fp4_peak"] = round(100.0 * tf / PEAK_FP4_TFLOPS, 2)
+        agg = qb / (qt * 1e-3) / 1e9
+        res[f"{prefix}quant_all6_ms"] = round(qt, 4)
+        res[f"{prefix}quant_all6_gbs"] = round(agg, 1)
+        res[f"{prefix}quant_all6_pct_of_hbm_peak"] = round(100.0 * agg / PEAK_HBM_GBS, 2)
+        return res, ms
 
 
-def cpu_baseline(layer, rows: int):
-    """The CPU oracle as it stands, on a bounded sample of the same step, extrapolated to the full
-    step: each of the six quantizations on its first `rows` source rows, and each GEMM on a
-    16 x 512 block of outputs. Returns the whole-step rate in TFLOP/s."""
+def timed_steps(layer, torch, steps):
+    """Runs `steps` steps with events around every launch; returns the events."""
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(layer.LAUNCHES) + 1)]
+           for _ in range(steps)]
+    for e in evs:
+        layer.step(e)
+    return evs
+
+
+def llama8b_components(mx, wl, torch, steps: int = 5):
+    """Outside the timed step: the Llama-3.1-8B up-projection step (T=8192, K=4096, N=14336;
+    floor scale, RNE; Wgrad with deterministic Hadamard along T), every launch timed."""
+    layer = Layer(mx, wl, "llama8b_up")
+    layer.step()
+    torch.cuda.synchronize()
+    evs = timed_steps(layer, torch, steps)
+    torch.cuda.synchronize()
+    res, _ = layer.launch_report(evs, prefix="llama8b_")
+    res["llama8b_workload"] = layer.desc
+    del layer
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_threads() -> int:
+    """Host threads the oracle may use: the CPUs this process may run on, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def cpu_baseline(layer, gemm_rows: int = 64, gemm_elements: int = 1024):
+    """The CPU oracle as it stands, timed on this host beside the GPU step.
+
+    Quantize: the threaded oracle over each of the step's six operand quantizations on the full
+    tensors (every thread gets at least one 32-row piece), as elements/s and GB/s of algorithmic
+    traffic (bf16 in, packed codes and scales out).
+    GEMM: for each of the three products, the float64 oracle on `gemm_rows` random full output
+    rows (every column) and separately on `gemm_elements` random single outputs. The full GEMM's
+    time is extrapolated from the row sample: dequantization scales with the operand elements
+    (M + N) * K, the float64 products with the output rows M.
+    Returns the whole-step rate in TFLOP/s with the pieces it was built from."""
     import numpy as np
+    import threadpoolctl
     from oracle import oracle as orc
     import workloads as wl
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    threads = max(1, min(threads, os.cpu_count() or 1, 16))
+    threads = cpu_threads()
     L = layer
+    rng = np.random.default_rng(2024)
+    quant = {}
     total = 0.0
-    specs = [("X", L.X, 1, L.fprop_q), ("W", L.W, 1, L.fprop_q), ("dY", L.dY, 1, L.dgrad_q),
-             ("W", L.W, 0, L.dgrad_q), ("dY", L.dY, 0, L.wgrad_q), ("X", L.X, 0, L.wgrad_q)]
-    for key, src, axis, (had, mask, rule, rnd) in specs:
-        r = min(rows, src.shape[0])
-        r -= r % 32
-        sample = wl.host_input(src[:r])
+    host = {}
+    specs = [("Xq", "X", 1, L.fprop_q), ("Wq", "W", 1, L.fprop_q), ("dYq", "dY", 1, L.dgrad_q),
+             ("Wt", "W", 0, L.dgrad_q), ("dYt", "dY", 0, L.wgrad_q), ("Xt", "X", 0, L.wgrad_q)]
+    for name, key, axis, (had, mask, rule, rnd) in specs:
+        if key not in host:
+            host[key] = wl.host_input(getattr(L, key))
+        x = host[key]
         t0 = time.perf_counter()
-        orc.quantize(sample, axis=axis, scale_rule=rule, round_mode=rnd, hadamard=had,
+        orc.quantize(x, axis=axis, scale_rule=rule, round_mode=rnd, hadamard=had,
                      sign_mask=mask, seed=L.seeds[key], nthreads=threads)
-        total += (time.perf_counter() - t0) * src.shape[0] / r
-    gm, gn = 16, 512
+        dt = time.perf_counter() - t0
+        total += dt
+        n = x.size
+        quant[name] = {"elements": n, "s": round(dt, 3), "elements_per_s": round(n / dt, 1),
+                       "GB_per_s": round(n * (2 + 0.5 + 1 / 32) / dt / 1e9, 3)}
+    host.clear()
     b = L.buf
-    for name, (aq, as_), (bq, bs), M, N, K in [
-            ("fprop", b["Xq"], b["Wq"], L.T, L.N, L.K), ("dgrad", b["dYq"], b["Wt"], L.T, L.K, L.N),
-            ("wgrad", b["dYt"], b["Xt"], L.N, L.K, L.T)]:
-        ha, hsa = aq[:gm].cpu().numpy(), as_[:gm].cpu().numpy()
-        hb, hsb = bq[:gn].cpu().numpy(), bs[:gn].cpu().numpy()
-        t0 = time.perf_counter()
-        orc.gemm(ha, hsa, 1, hb, hsb, 1, gm, gn, K, L.alpha[name])
-        total += (time.perf_counter() - t0) * (M * N) / (gm * gn)
+    gemm = {}
+    with threadpoolctl.threadpool_limits(limits=threads):
+        blas = [d["num_threads"] for d in threadpoolctl.threadpool_info()
+                if d.get("user_api") == "blas"]
+        for name, (aq, as_), (bq, bs), M, N, K in [
+                ("fprop", b["Xq"], b["Wq"], L.T, L.N, L.K),
+                ("dgrad", b["dYq"], b["Wt"], L.T, L.K, L.N),
+                ("wgrad", b["dYt"], b["Xt"], L.N, L.K, L.T)]:
+            ha, hsa = aq.cpu().numpy(), as_.cpu().numpy()
+            hb, hsb = bq.cpu().numpy(), bs.cpu().numpy()
+            rows = np.sort(rng.choice(M, size=min(gemm_rows, M), replace=False))
+            tm = {}
+            orc.gemm(ha, hsa, 1, hb, hsb, 1, M, N, K, L.alpha[name], rows=rows, timings=tm)
+            r = len(rows)
+            deq_rate = (r + N) * K / tm["dequant_s"]
+            mm_flops = 2.0 * 2 * r * N * K  # the signed and the absolute product
+            full_s = (M + N) * K / deq_rate + tm["matmul_s"] * M / r
+            em = rng.integers(0, M, gemm_elements)
+            en = rng.integers(0, N, gemm_elements)
+            t0 = time.perf_counter()
+            for m, n in zip(em, en):
+                orc.gemm(ha, hsa, 1, hb, hsb, 1, M, N, K, L.alpha[name], rows=[m], cols=[n])
+            el_s = (time.perf_counter() - t0) / gemm_elements
+            total += full_s
+            gemm[name] = {
+                "sample_rows": r, "dequant_s": round(tm["dequant_s"], 3),
+                "dequant_elements_per_s": round(deq_rate, 1),
+                "matmul_s": round(tm["matmul_s"], 3),
+                "matmul_GFLOP_per_s": round(mm_flops / tm["matmul_s"] / 1e9, 2),
+                "full_gemm_extrapolated_s": round(full_s, 2),
+                "single_element_us": round(el_s * 1e6, 1),
+            }
     flops = sum(L.flops.values())
-    return {"value": flops / total / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": (f"oracle quantize of the first {rows} source rows of each of the 6 operand "
-                       f"quantizations and oracle GEMM of a {gm}x{gn} output block of each GEMM, "
-                       f"times extrapolated by element count to the full step "
-                       f"(extrapolated full step {total:.1f} s)"),
-            "np_threads_note": "numpy float64 matmul uses the BLAS thread pool",
-            "_numpy": np.__version__}
+    return {"value": round(flops / total / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"oracle quantize of all six operand quantizations on the full tensors "
+                       f"({threads} threads); oracle float64 GEMM on {gemm_rows} random full "
+                       f"output rows and {gemm_elements} random single outputs of each product, "
+                       f"full GEMM time extrapolated by (M+N)*K for dequantization and by M for "
+                       f"the products; whole step {total:.1f} s"),
+            "blas_threads": blas[0] if blas else None,
+            "quantize": quant, "gemm": gemm}
 
 
 def load_traffic(launch_flops_key: str, workload: str):
@@ -383,9 +496,11 @@ def mfma_ceiling(torch, workgroups: int = 2048, iters: int = 1000, reps: int = 3
 
 def block_variants(mx, wl, torch, reps: int = 5):
     """Outside the timed step: the tile-size variants on the 2-D workload (W 14336x4096, X
-    8192x4096, bf16, ceil scale, RNE): 8x8, 32x32 and 64x64 quantization with both code layouts,
-    Fprop on W's 32x32 and 64x64 scales against 1x32, and the 1D scale-mismatch map of X with its
-    summary (the share of elements whose two 1D scales differ, and the mean |difference|)."""
+    8192x4096, dY 8192x14336, bf16, ceil scale, RNE unless stated): 8x8, 32x32 and 64x64
+    quantization with both code layouts, Fprop on W's 32x32 and 64x64 scales against 1x32, Dgrad
+    and Wgrad consuming the transposed 32x32 tiles of W and of dY (SR) with no requantization,
+    and the 1D scale-mismatch map of X with its summary (the share of elements whose two 1D
+    scales differ, and the mean |difference|)."""
     d = wl.blocks_2d(device="cuda")
     X, W = d["X"], d["W"]
     N, K = W.shape
@@ -422,6 +537,26 @@ def block_variants(mx, wl, torch, reps: int = 5):
         ms = timed(lambda: mx.mx_gemm_fprop(xq, xs, 1, wq, ws, g, out=y))
         res[f"fprop_w_{name}_ms"] = round(ms, 4)
         res[f"fprop_w_{name}_tflops"] = round(flops / (ms * 1e-3) / 1e12, 1)
+    # Dgrad and Wgrad on the transposed 32x32 tiles without requantization: dY 8192x14336 in
+    # 32x32 tiles with SR, W's transposed tile codes, X 1x32 along T
+    dY = d["dY"]
+    dc, ds, dct, dst = mx.mx_quantize_2d(dY, scale_rule=1, round=1, seed=wl.SR_SEED + 2)
+    ms = timed(lambda: mx.mx_quantize_2d(dY, scale_rule=1, round=1, seed=wl.SR_SEED + 2,
+                                         codes=dc, scales=ds, codes_t=dct, scales_t=dst))
+    res["quant_2d_dY_sr_ms"] = round(ms, 4)
+    res["quant_2d_dY_sr_gbs"] = round((T * N * 3 + ds.numel() + dst.numel()) / (ms * 1e-3) / 1e9, 1)
+    xtq, xts = mx.mx_quantize(X, axis=0, scale_rule=1)
+    dx = torch.empty((T, K), dtype=torch.bfloat16, device="cuda")
+    dw = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
+    _, _, wct, wst = ops[32]
+    for name, fn in (("dgrad", lambda: mx.mx_gemm_dgrad(dc, ds, 32, wct, wst, 32, out=dx)),
+                     ("wgrad", lambda: mx.mx_gemm_wgrad(dct, dst, 32, xtq, xts, 1, out=dw))):
+        ms = timed(fn)
+        tf = flops / (ms * 1e-3) / 1e12
+        res[f"tiles32_{name}_ms"] = round(ms, 4)
+        res[f"tiles32_{name}_tflops"] = round(tf, 1)
+        res[f"tiles32_{name}_pct_of_fp4_peak"] = round(100.0 * tf / PEAK_FP4_TFLOPS, 2)
+    del dc, ds, dct, dst, xtq, xts, dx, dw
     m = mx.mx_scale_mismatch_map(X)
     ms = timed(lambda: mx.mx_scale_mismatch_map(X, out=m))
     res["mismatch_map_ms"] = round(ms, 4)
@@ -480,9 +615,14 @@ def write_traffic(fetch_csv: str, write_csv: str, workload: str):
     wf = COPY_BYTES / (copy_value(write) * 1024.0)
 
     def gemm_launches(table):
-        # the MXFP4 GEMM with plain output (template arguments ..., QOUT false, A and B formats
-        # 4), not the quantizing epilogue or the MXFP8 kernel; the step's launches come first
-        vals = [vs for name, vs in table.items() if re.search(r"gemm_mx\w*<[^>]*false, 4, 4>", name)]
+        # the MXFP4 GEMM with plain output: the ping-pong kernel that serves reductions of a
+        # multiple of 1024 (all three of this workload), else the streaming kernel with template
+        # arguments ..., QOUT false, A and B formats 4 (not the quantizing epilogue or MXFP8);
+        # the step's launches come first
+        vals = [vs for name, vs in table.items() if "gemm_mx_pp_kernel" in name]
+        if not vals:
+            vals = [vs for name, vs in table.items()
+                    if re.search(r"gemm_mx\w*<[^>]*false, 4, 4>", name)]
         if len(vals) != 1 or len(vals[0]) < 3 * TRAFFIC_STEPS:
             raise SystemExit("expected one MXFP4 GEMM kernel with the step's launches first")
         per = {k: [] for k in TRAFFIC_ORDER}
@@ -547,23 +687,18 @@ def main():
     torch.cuda.synchronize()
     print(f"bench: warmup done, timing {args.steps} steps", file=sys.stderr, flush=True)
 
-    evs = [{k: torch.cuda.Event(enable_timing=True) for k in ("q0", "q1", "w0", "w1")}
-           for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        layer.step(evs[i])
+    evs = timed_steps(layer, torch, args.steps)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_step = 1e3 * elapsed / args.steps
-    wgrad_ms = sum(e["w0"].elapsed_time(e["w1"]) for e in evs) / args.steps
-    quant_ms = sum(e["q0"].elapsed_time(e["q1"]) for e in evs) / args.steps
+    launches, ms = layer.launch_report(evs)
+    wgrad_ms = ms["wgrad"]
 
     flops = sum(layer.flops.values())
     value = flops / (ms_step * 1e-3) / 1e12
     wgrad_tflops = layer.flops["wgrad"] / (wgrad_ms * 1e-3) / 1e12
-    qelems = layer.T * layer.K
-    quant_gbs = qelems * QUANT_BYTES_PER_ELEM / (quant_ms * 1e-3) / 1e9
     traffic = load_traffic("wgrad_hbm_bytes_per_launch", args.workload)
     ceiling = mfma_ceiling(torch)  # after the timed steps, outside the timed region
 
@@ -586,13 +721,14 @@ def main():
             "wgrad_gemm_ms": round(wgrad_ms, 4),
             "wgrad_gemm_tflops": round(wgrad_tflops, 2),
             "wgrad_pct_of_fp4_peak": round(100.0 * wgrad_tflops / PEAK_FP4_TFLOPS, 2),
-            "hadamard_quant_kernel": f"mx_quantize {layer.T}x{layer.K} bf16 along rows",
-            "hadamard_quant_ms": round(quant_ms, 4),
-            "hadamard_quant_gbs": round(quant_gbs, 1),
-            "hadamard_quant_pct_of_hbm_peak": round(100.0 * quant_gbs / PEAK_HBM_GBS, 2),
+            "hadamard_quant_kernel": "all six mx_quantize launches of the step (rows and columns)",
+            "hadamard_quant_ms": launches["quant_all6_ms"],
+            "hadamard_quant_gbs": launches["quant_all6_gbs"],
+            "hadamard_quant_pct_of_hbm_peak": launches["quant_all6_pct_of_hbm_peak"],
+            **launches,
         },
         "roofline": {
-            "kernel": "gemm_mx_stream_kernel (Wgrad launch)",
+            "kernel": "gemm_mx_pp_kernel (Wgrad launch)",
             "bound": "mfma",
             "achieved": round(wgrad_tflops, 2),
             "peak": PEAK_FP4_TFLOPS,
@@ -612,11 +748,11 @@ def main():
         out["components"].update(quant_stream(mx, wl, torch))
         out["components"].update(mxfp8_attention(mx, wl, torch))
         out["components"].update(block_variants(mx, wl, torch))
+        if args.workload != "llama8b_up":
+            out["components"].update(llama8b_components(mx, wl, torch))
     if not args.no_cpu_baseline:
-        print("bench: timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        cb = cpu_baseline(layer, args.cpu_sample_rows)
-        cb.pop("_numpy", None)
-        out["cpu_baseline"] = cb
+        print("bench: timing the CPU oracle beside the step", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(layer, args.cpu_gemm_rows, args.cpu_gemm_elements)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

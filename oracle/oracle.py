@@ -24,6 +24,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import time
 
 import numpy as np
 
@@ -310,14 +311,21 @@ def dequantize_f64(codes: np.ndarray, scales: np.ndarray, rows: int, k: int, g: 
 
 
 def gemm(aq, as_, ga: int, bq, bs, gb: int, M: int, N: int, K: int, alpha_exp: int = 0,
-         rows=None, cols=None):
+         rows=None, cols=None, timings=None):
     """C[m][n] = 2^alpha * sum_k A[m][k] B[n][k] in float64, and the matching sum of |a_k b_k|.
-    rows / cols optionally select output rows / columns (sampled checks)."""
+    rows / cols optionally select output rows / columns (sampled checks). A dict passed as
+    timings receives the seconds spent dequantizing ("dequant_s") and in the two products
+    ("matmul_s")."""
+    t0 = time.perf_counter()
     A = dequantize_f64(aq, as_, M, K, ga, rows)
     B = dequantize_f64(bq, bs, N, K, gb, cols)
+    t1 = time.perf_counter()
     f = 2.0 ** alpha_exp
     C = (A @ B.T) * f
     Cabs = (np.abs(A) @ np.abs(B).T) * f
+    if timings is not None:
+        timings["dequant_s"] = t1 - t0
+        timings["matmul_s"] = time.perf_counter() - t1
     return C, Cabs
 
 

@@ -19,6 +19,7 @@ GEMM = "(anonymous namespace)::gemm_mx_stream_kernel<4, 4, 2, 8, 8, 1, false, 4,
 QOUT = "(anonymous namespace)::gemm_mx_stream_kernel<4, 4, 2, 8, 8, 1, true, 4, 4>(args)"
 FP8 = "(anonymous namespace)::gemm_mx_stream_kernel<4, 4, 2, 16, 2, 0, false, 0, 0>(args)"
 QUANT = "(anonymous namespace)::quant_rows_kernel<true, true, true, true>(args)"
+PP = "(anonymous namespace)::gemm_mx_pp_kernel(unsigned char const*, int)"
 COPY = "__amd_rocclr_copyBuffer"
 FETCH_KIB = {"fprop": 1_400_000.0, "dgrad": 1_500_000.0, "wgrad": 1_450_000.0}
 
@@ -42,9 +43,10 @@ def write_csv(path, counter, rows):
                         "Counter_Value": 1e12})
 
 
-def dispatches(value_of, copy_kib, steps=3, write_scale=None):
+def dispatches(value_of, copy_kib, steps=3, write_scale=None, gemm=GEMM, extra=()):
     """A run in dispatch order: per step, a quantizer and the three GEMMs; then the quantizing
-    epilogue and an MXFP8 GEMM (not the plain MXFP4 kernel), then the calibration copy."""
+    epilogue and an MXFP8 GEMM (not the plain MXFP4 kernel), `extra` launches, then the
+    calibration copy."""
     rows, d = [], 1
     for _ in range(steps):
         rows.append((d, QUANT, 123.0)); d += 1
@@ -52,8 +54,12 @@ def dispatches(value_of, copy_kib, steps=3, write_scale=None):
             v = value_of(name)
             if write_scale and name in write_scale:
                 v *= write_scale[name]
-            rows.append((d, GEMM, v)); d += 1
-    rows += [(d, QOUT, 9e9), (d + 1, FP8, 9e9), (d + 2, COPY, copy_kib), (d + 3, COPY, 10.0)]
+            rows.append((d, gemm, v)); d += 1
+    rows += [(d, QOUT, 9e9), (d + 1, FP8, 9e9)]
+    d += 2
+    for name in extra:
+        rows.append((d, name, 7e9)); d += 1
+    rows += [(d, COPY, copy_kib), (d + 1, COPY, 10.0)]
     return rows
 
 
@@ -64,11 +70,12 @@ def record_path(tmp_path, monkeypatch):
     return p
 
 
-def make_files(tmp_path, write_scale=None):
+def make_files(tmp_path, write_scale=None, **kw):
     fetch_csv, wr_csv = tmp_path / "fetch.csv", tmp_path / "write.csv"
     # the copy reads 1 GiB but FETCH_SIZE reports half of it (factor 2); WRITE_SIZE reports all
-    write_csv(fetch_csv, "FETCH_SIZE", dispatches(lambda n: FETCH_KIB[n], (1 << 30) / 2048.0))
-    write_csv(wr_csv, "WRITE_SIZE", dispatches(out_kib, (1 << 30) / 1024.0, write_scale=write_scale))
+    write_csv(fetch_csv, "FETCH_SIZE", dispatches(lambda n: FETCH_KIB[n], (1 << 30) / 2048.0, **kw))
+    write_csv(wr_csv, "WRITE_SIZE", dispatches(out_kib, (1 << 30) / 1024.0,
+                                               write_scale=write_scale, **kw))
     return str(fetch_csv), str(wr_csv)
 
 
@@ -80,8 +87,12 @@ def test_counter_values_sums_instances_in_dispatch_order(tmp_path):
     assert vals[COPY] == pytest.approx([4.0])
 
 
-def test_write_traffic_record(tmp_path, record_path, monkeypatch):
-    fetch_csv, wr_csv = make_files(tmp_path)
+@pytest.mark.parametrize("kw", [{}, {"gemm": PP}, {"gemm": PP, "extra": (GEMM,) * 12}],
+                         ids=["stream", "pingpong", "pingpong_then_stream"])
+def test_write_traffic_record(tmp_path, record_path, monkeypatch, kw):
+    # the ping-pong kernel's launches are the step's when present, whatever streaming-kernel
+    # launches follow in the run
+    fetch_csv, wr_csv = make_files(tmp_path, **kw)
     monkeypatch.setattr(bench, "sha", lambda path: "0123456789abcdef")
     bench.write_traffic(fetch_csv, wr_csv, "llama70b_down")
     rec = json.load(open(record_path))
@@ -133,3 +144,38 @@ def test_write_traffic_other_workload(tmp_path, record_path):
     fetch_csv, wr_csv = make_files(tmp_path)
     with pytest.raises(SystemExit):
         bench.write_traffic(fetch_csv, wr_csv, "llama8b_up")
+
+
+def test_cpu_baseline_on_a_small_layer():
+    """The CPU baseline runs the oracle as it stands on a host-side stand-in for the layer and
+    reports the pieces its whole-step figure is built from."""
+    import torch
+    T, K, N = 256, 1024, 128
+    g = torch.Generator().manual_seed(0)
+
+    class Small:
+        pass
+    L = Small()
+    L.T, L.K, L.N = T, K, N
+    L.X = torch.randn((T, K), generator=g).to(torch.bfloat16)
+    L.W = torch.randn((N, K), generator=g).to(torch.bfloat16)
+    L.dY = torch.randn((T, N), generator=g).to(torch.bfloat16)
+    L.fprop_q = L.dgrad_q = L.wgrad_q = (1, 0x1234, 1, 1)
+    L.seeds = {"X": 1, "W": 2, "dY": 3}
+    L.alpha = {"fprop": -5, "dgrad": -5, "wgrad": -5}
+    L.flops = {"fprop": 2.0 * T * N * K, "dgrad": 2.0 * T * K * N, "wgrad": 2.0 * N * K * T}
+    u8 = lambda *s: torch.randint(0, 256, s, generator=g, dtype=torch.uint8)  # noqa: E731
+    sc = lambda *s: torch.randint(120, 134, s, generator=g, dtype=torch.uint8)  # noqa: E731
+    L.buf = {"Xq": (u8(T, K // 2), sc(T, K // 32)), "Wq": (u8(N, K // 2), sc(N, K // 32)),
+             "dYq": (u8(T, N // 2), sc(T, N // 32)), "Wt": (u8(K, N // 2), sc(K, N // 32)),
+             "dYt": (u8(N, T // 2), sc(N, T // 32)), "Xt": (u8(K, T // 2), sc(K, T // 32))}
+    cb = bench.cpu_baseline(L, gemm_rows=8, gemm_elements=16)
+    assert cb["kind"] == "oracle" and cb["unit"] == "TFLOP/s" and cb["value"] > 0
+    assert cb["cores"] == bench.cpu_threads()
+    assert set(cb["quantize"]) == {"Xq", "Wq", "dYq", "Wt", "dYt", "Xt"}
+    assert cb["quantize"]["Xq"]["elements"] == T * K
+    for name in ("fprop", "dgrad", "wgrad"):
+        gm = cb["gemm"][name]
+        assert gm["sample_rows"] == 8 and gm["matmul_GFLOP_per_s"] > 0
+        assert gm["full_gemm_extrapolated_s"] > 0
+    json.dumps(cb)

@@ -120,7 +120,7 @@ def llama8b(mx):
 def test_llama8b_quantize_sampled(orc, llama8b, name, src, axis, had):
     d, q, _ = llama8b
     x = d[src]
-    check_quant_rows(orc, x, *q[name], axis, row_samples(x.shape[0], seed=len(name)),
+    check_quant_rows(orc, x, *q[name], axis, row_samples(x.shape[0], count=6, seed=len(name)),
                      scale_rule=0, round_mode=0, hadamard=had, sign_mask=0)
 
 
@@ -130,6 +130,15 @@ def test_llama8b_gemm_sampled(orc, llama8b, gemm):
     a, b, o, alpha = {"fprop": ("Xq", "Wq", "Y", 0), "dgrad": ("dYq", "Wt", "dX", 0),
                       "wgrad": ("dYt", "Xt", "dW", -5)}[gemm]
     check_gemm_sampled(orc, out[o], *q[a], 1, *q[b], 1, alpha, seed=len(gemm))
+
+
+def test_llama8b_wgrad_fp32_full_k(mx, orc, llama8b):
+    """Wgrad's reduction runs over all T = 8192 tokens; with fp32 output the accumulated sum is
+    held to 2^-20 * sum|ab| (no bf16 bracket to hide in) on 16 rows x 1024 columns."""
+    _, q, _ = llama8b
+    dW = mx.mx_gemm_wgrad(*q["dYt"], 1, *q["Xt"], 1, alpha_exp=-5, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    check_gemm_sampled(orc, dW, *q["dYt"], 1, *q["Xt"], 1, -5, seed=11, nrows=16, ncols=1024)
 
 
 # ------------------------------------------------------------------------------------------------
@@ -211,7 +220,7 @@ def test_llama70b_quantize_sampled(orc, llama70b, name, src, axis):
     L = llama70b
     had, mask, rule, rnd = L.fprop_q
     x = getattr(L, src)
-    check_quant_rows(orc, x, *L.buf[name], axis, row_samples(x.shape[0], count=1, seed=axis),
+    check_quant_rows(orc, x, *L.buf[name], axis, row_samples(x.shape[0], count=3, seed=axis),
                      scale_rule=rule, round_mode=rnd, hadamard=had, sign_mask=mask,
                      seed=L.seeds[src])
 
@@ -223,3 +232,16 @@ def test_llama70b_gemm_sampled(orc, llama70b, gemm):
                "wgrad": ("dYt", "Xt", L.dW)}[gemm]
     check_gemm_sampled(orc, o, *L.buf[a], 1, *L.buf[b], 1, L.alpha[gemm], seed=len(gemm),
                        nrows=4, ncols=512)
+
+
+@pytest.mark.parametrize("gemm", ["fprop", "dgrad", "wgrad"])
+def test_llama70b_gemm_fp32_full_k(mx, orc, llama70b, gemm):
+    """The same operands with fp32 output, so the full-length sums (Fprop K = 28672, Dgrad
+    K = 8192, Wgrad K = T = 16384) are held to 2^-20 * sum|ab| on 16 rows x 1024 columns."""
+    L = llama70b
+    a, b = {"fprop": ("Xq", "Wq"), "dgrad": ("dYq", "Wt"), "wgrad": ("dYt", "Xt")}[gemm]
+    fn = getattr(mx, "mx_gemm_" + gemm)
+    o = fn(*L.buf[a], 1, *L.buf[b], 1, alpha_exp=L.alpha[gemm], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    check_gemm_sampled(orc, o, *L.buf[a], 1, *L.buf[b], 1, L.alpha[gemm], seed=7 + len(gemm),
+                       nrows=16, ncols=1024)

@@ -446,3 +446,30 @@ def test_gemm_scale_shift_doubles_output(orc):
     C3, _ = orc.gemm(aq, s2, 32, bq, bs, 1, M, N, K)
     C4, _ = orc.gemm(aq, np.repeat(s2, 32, axis=0), 1, bq, bs, 1, M, N, K)
     assert np.array_equal(C3, C4)
+
+
+@pytest.mark.parametrize("nthreads", [2, 3, 8])
+def test_threaded_driver_equals_one_thread(orc, nthreads):
+    """The threaded driver only splits the row range into 32-row pieces; every option set
+    (1x32 along either axis, Hadamard with random signs, SR, 32x32 tiles) and a row range whose
+    piece count does not divide by the thread count give the same bytes as one thread."""
+    rng = np.random.default_rng(31)
+    x = (rng.standard_t(3, size=(32 * 37, 96)) * 0.2).astype(np.float32)
+    mask = 0x9E3779B9
+    for axis in (1, 0):
+        for rr in (None, (64, 32 * 30)):
+            kw = dict(axis=axis, scale_rule=1, round_mode=1, hadamard=1, sign_mask=mask, seed=77,
+                      row_range=rr)
+            one = orc.quantize(x, nthreads=1, **kw)
+            many = orc.quantize(x, nthreads=nthreads, **kw)
+            for a, b in zip(one, many):
+                assert np.array_equal(a, b)
+    for rr in (None, (32, 32 * 33)):
+        one = orc.quantize_2d(x, scale_rule=1, round_mode=1, seed=5, row_range=rr, nthreads=1)
+        many = orc.quantize_2d(x, scale_rule=1, round_mode=1, seed=5, row_range=rr,
+                               nthreads=nthreads)
+        for a, b in zip(one, many):
+            assert np.array_equal(a, b)
+    # the untouched rows outside a range stay zero, and the range itself is fully written
+    c, s = orc.quantize(x, axis=1, row_range=(64, 128), nthreads=nthreads)
+    assert not c[:64].any() and not c[128:].any() and s[64:128].all()
