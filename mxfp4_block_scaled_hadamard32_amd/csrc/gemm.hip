@@ -950,7 +950,13 @@ void gemm_mx_stream_kernel(const uint8_t* __restrict__ A, const uint8_t* __restr
 // group 1's M(k-1)) and one quarter of a scale group, waited for at the end of its C(k); wave s
 // of group 1, once its own M(k) reads of stage k % 2 are complete, issues the 64 B rows it and
 // wave s of group 0 read (group 0's M(k) is a phase older), for step k+2 into that stage, and
-// waits for them at the end of its M(k+1). Steps 0 and 1 and scale group 0 are loaded up front.
+// waits for them at the end of its M(k+1). Steps 0 and 1 and scale group 0 are loaded up front:
+// for a workgroup's first tile before it, for each later tile at the end of the tile before.
+// There step 0 and scale group 0 go out as soon as the last compute phase is done, the epilogue
+// stages the output through stage 1 only, and step 1 and the first quarter of scale group 1 go
+// out after it, ahead of the output stores. The next tile's first waits count those stores as
+// still in flight (a wave's vector memory operations complete in issue order), so the stores
+// drain under its first compute phase instead of ahead of it.
 // ---------------------------------------------------------------------------------------------
 namespace pp {
 constexpr int kThreads = 512;
@@ -961,9 +967,25 @@ constexpr int kGrpRow = 32;                  // scale bytes per row per group (4
 constexpr int kGrpOp = 256 * kGrpRow;        // 8 KiB per operand
 constexpr int kGrp = 2 * kGrpOp;             // A then B
 constexpr int kLds = 2 * kStage + 2 * kGrp;  // 160 KiB
-constexpr int kBf16Pitch = 256 * 2 + 16;     // epilogue staging row pitch (bf16)
-constexpr int kF32Pitch = 256 * 4 + 16;      // epilogue staging row pitch (fp32, 128-row passes)
-static_assert(256 * kBf16Pitch <= kLds && 128 * kF32Pitch <= kLds, "staging fits in LDS");
+// epilogue staging in stage 1: 128-row passes of bf16 rows (512 B) or 64-row passes of fp32
+// rows (1 KiB); the 16-byte chunks of row r sit at chunk ^ (r % 32), so that a column of rows
+// written by one instruction and a row read by one instruction both spread over all banks
+static_assert(kStage == 128 * 512 && kStage == 64 * 1024, "staging passes");
+__device__ __forceinline__ uint32_t stage_chunk(int row, int chunk) {
+  return (uint32_t)(chunk ^ (row & 31)) * 16u;
+}
+
+// s_waitcnt vmcnt with a count known only at run time (uniform), from the values used below
+__device__ __forceinline__ void wait_vmcnt_upto(int n) {
+  switch (n) {
+    case 25: wait_vmcnt<25>(); break;
+    case 24: wait_vmcnt<24>(); break;
+    case 16: wait_vmcnt<16>(); break;
+    case 9: wait_vmcnt<9>(); break;
+    case 8: wait_vmcnt<8>(); break;
+    default: wait_vmcnt<0>(); break;
+  }
+}
 
 __device__ __forceinline__ void barrier() {
   __builtin_amdgcn_sched_barrier(0);
@@ -1021,11 +1043,16 @@ void gemm_mx_pp_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
   const int nblocks = nbm * nbn;
   const int64_t kbytes = K / 2, nkb = K / 32;
   const int n = (int)(K / 256);  // steps per tile, a multiple of 4
+  __builtin_assume(n >= 4);
 
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int s = w & 3, g = w >> 2;           // index within the group, and the group
   const int wm = g, wn = s;
   const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(smem);
+  // output stores the previous tile issued after the last loads of this tile (0 for the first
+  // tile, and after a partial tile, whose stores are not all issued), and the loads and stores
+  // that may still be in flight when this tile starts (0 for the first tile)
+  int nst_prev = 0, in_flight = 0;
 
   // Direct-to-LDS loads of wave s of a group (lane-dependent parts; the rest is scalar):
   //  * A code load q (0..7, group 0) of a step fills 1 KiB block b = s + 4q of the A stage tile:
@@ -1046,9 +1073,12 @@ void gemm_mx_pp_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
   };
 
   for (int tile = blockIdx.x; tile < nblocks; tile += gridDim.x) {
-    int t = threadIdx.x;
-    asm volatile("" : "+v"(t));  // per tile: keep lane setup out of the loop-carried state
-    const int lane = t & 63;
+    // the lane index from the execution mask (not threadIdx, which would have to be kept in a
+    // register through the tile loop); per tile, so that the lane setup stays out of the
+    // loop-carried state
+    uint32_t zero = 0;
+    asm volatile("" : "+s"(zero));
+    const int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, zero));
     const int frow = lane & 31, h = lane >> 5;
     int64_t m0, n0;
     tile_origin(tile, nbm, nbn, m0, n0);
@@ -1073,21 +1103,24 @@ void gemm_mx_pp_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
     // the k offset is scalar.
     // (The lane offsets pass through an empty asm at each use, so that the eight per-load
     // offsets are recomputed there instead of being held in registers across the loop.)
+    // (The wave's LDS base also passes through an empty asm, so that the eight destinations are
+    // formed at each use rather than held in scalar registers.)
     auto issue_codes = [&](const TileRes& r, int j, int op) {
-      const uint32_t st = lds0 + (j & 1) * kStage;
       if (op == 0) {
+        uint32_t st = lds0 + 1024 * s;
         int v0 = voff0;
-        asm volatile("" : "+v"(v0));
+        asm volatile("" : "+v"(v0), "+s"(st));
+        st += (j & 1) * kStage;
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
-          dma_b128(r.ra, st + 1024 * (s + 4 * q), v0 + q * 32 * (int)kbytes, j * kRow);
+        for (int q = 0; q < 8; ++q) dma_b128(r.ra, st + 4096 * q, v0 + q * 32 * (int)kbytes, j * kRow);
       } else {
+        uint32_t st = lds0 + kTile + 8192 * s;
         int v0 = voffb0, v1 = voffb1;
-        asm volatile("" : "+v"(v0), "+v"(v1));
+        asm volatile("" : "+v"(v0), "+v"(v1), "+s"(st));
+        st += (j & 1) * kStage;
 #pragma unroll
         for (int q = 0; q < 8; ++q)
-          dma_b128(r.rb, st + kTile + 1024 * (8 * s + q), ((q & 1) ? v1 : v0) + 8 * q * (int)kbytes,
-                   j * kRow);
+          dma_b128(r.rb, st + 1024 * q, ((q & 1) ? v1 : v0) + 8 * q * (int)kbytes, j * kRow);
       }
     };
     auto issue_quarter = [&](const TileRes& r, int G, int p) {
@@ -1103,17 +1136,24 @@ void gemm_mx_pp_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
 
     // Steps 0 and 1 of a tile, scale group 0 and the first quarter of group 1: group 0 loads
     // A and the scales, group 1 loads B. The first tile of a workgroup issues them here, later
-    // tiles at the end of the previous tile.
-    auto prologue = [&](const TileRes& r) {
+    // tiles at the end of the previous tile (step 0 and group 0 before its epilogue, the rest
+    // after it).
+    auto prologue0 = [&](const TileRes& r) {
       issue_codes(r, 0, g);
-      if (n > 1) issue_codes(r, 1, g);
       if (g == 0) {
 #pragma unroll
         for (int p = 0; p < 4; ++p) issue_quarter(r, 0, p);
-        if (4 < n) issue_quarter(r, 1, 0);
       }
     };
-    if (tile == (int)blockIdx.x) prologue(R);
+    auto prologue1 = [&](const TileRes& r) {
+      issue_codes(r, 1, g);
+      if (g == 0 && 4 < n) issue_quarter(r, 1, 0);
+    };
+    const bool first = tile == (int)blockIdx.x;
+    if (first) {
+      prologue0(R);
+      prologue1(R);
+    }
 
     // per-lane LDS offsets of the fragment and scale reads
     const int phi = (frow >> 1) & 7;
@@ -1136,7 +1176,8 @@ void gemm_mx_pp_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
 
     // memory phase of step k: fragments and scale words into registers (plus, in group 0, the
     // loads of step k + 1); ends with this wave's reads complete
-    auto mem_phase = [&](int k) {
+    auto mem_phase = [&](int k, auto step0, auto grp) {
+      constexpr int G = decltype(grp)::value;
       const uint8_t* st = smem + (k & 1) * kStage;
 #pragma unroll
       for (int ss = 0; ss < 4; ++ss) {
@@ -1156,13 +1197,16 @@ void gemm_mx_pp_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
 #pragma unroll
       for (int j = 0; j < 2; ++j)
         sb[j] = *reinterpret_cast<const uint32_t*>(smem + sb_row + 1024 * j + sofs);
-      if (g == 0 && k >= 1 && k + 1 < n) {
+      if (G == 0 && k >= 1 && k + 1 < n) {
         issue_codes(R, k + 1, 0);
         if (k + 4 < n) issue_quarter(R, (k + 4) >> 2, (k + 4) & 3);  // groups of this tile only
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage k are done
-      if (g == 1) {
-        wait_vmcnt<0>();  // B of step k + 1 has landed
+      if constexpr (G == 1) {
+        // B of step k + 1 has landed (at k = 0 the previous tile's output stores, issued after
+        // it, may still be in flight)
+        if constexpr (decltype(step0)::value) wait_vmcnt_upto(nst_prev);
+        else wait_vmcnt<0>();
         if (k + 2 < n) issue_codes(R, k + 2, 1);
       }
     };
@@ -1180,12 +1224,25 @@ void gemm_mx_pp_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
       __builtin_amdgcn_s_setprio(0);
     };
 
-    wait_vmcnt<0>();  // this tile's steps 0 and 1 and scale group 0
+    // this tile's step 0 and scale group 0 have landed: everything of a first tile; for a
+    // later tile all but step 1 (8 loads), the quarter of group 1 (group 0, one load) and the
+    // stores after them
+    wait_vmcnt_upto(in_flight);
     barrier();
+    // step 0 is peeled off the loops: its waits let the previous tile's stores stay in flight
+    using Step0 = std::integral_constant<bool, true>;
+    using StepK = std::integral_constant<bool, false>;
+    using Grp0 = std::integral_constant<int, 0>;
+    using Grp1 = std::integral_constant<int, 1>;
     if (g == 0) {
+      mem_phase(0, Step0{}, Grp0{});
+      barrier();
+      compute_phase();
+      wait_vmcnt_upto(nst_prev);  // A of step 1 and the scale quarter, not the stores after them
+      barrier();
 #pragma unroll 1
-      for (int k = 0; k < n; ++k) {
-        mem_phase(k);
+      for (int k = 1; k < n; ++k) {
+        mem_phase(k, StepK{}, Grp0{});
         barrier();
         compute_phase();
         wait_vmcnt<0>();  // A of step k + 1 and the scale quarter have landed
@@ -1194,66 +1251,49 @@ void gemm_mx_pp_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
       barrier();  // group 1 computes step n - 1
     } else {
       barrier();  // group 0 reads step 0
+      mem_phase(0, Step0{}, Grp1{});
+      barrier();
+      compute_phase();
+      barrier();
 #pragma unroll 1
-      for (int k = 0; k < n; ++k) {
-        mem_phase(k);
+      for (int k = 1; k < n; ++k) {
+        mem_phase(k, StepK{}, Grp1{});
         barrier();
         compute_phase();
         barrier();
       }
     }
-    // both groups are past their last reads of the stages and scale groups: LDS is free
+    // both groups are past their last reads of the stages and scale groups: the next tile's
+    // step 0 and scale group 0 go out now
+    const int next = tile + (int)gridDim.x;
+    const bool has_next = next < nblocks;
+    if (has_next) {
+      int64_t nm0, nn0;
+      tile_origin(next, nbm, nbn, nm0, nn0);
+      prologue0(tile_res(A, As, lga, B, Bs, lgb, M, N, K, nm0, nn0));
+    }
 
     // Epilogue: acc[i][j][r] = C[m][n], m = 128 wm + 32 i + (lane % 32),
     //                                   n = 64 wn + 32 j + 8 (r / 4) + 4 (lane / 32) + r % 4.
-    // The tile goes through LDS so that stores write whole rows; the row values are read back
-    // into registers first, so the next tile's first loads can go out before the stores.
-    const int next = tile + (int)gridDim.x;
-    auto prologue_next = [&]() {
-      if (next < nblocks) {
+    // The tile goes through stage 1 so that stores write whole rows; the row values are read
+    // back into registers first, so that the next tile's step 1 can go out before the stores.
+    uint8_t* const stg = smem + kStage;
+    auto step1_next = [&]() {
+      if (has_next) {
         int64_t nm0, nn0;
         tile_origin(next, nbm, nbn, nm0, nn0);
-        prologue(tile_res(A, As, lga, B, Bs, lgb, M, N, K, nm0, nn0));
+        prologue1(tile_res(A, As, lga, B, Bs, lgb, M, N, K, nm0, nn0));
       }
     };
     const bool full = m0 + 256 <= M && n0 + 256 <= N;
-    if (out_bf16) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int rq = 0; rq < 4; ++rq) {
-            const int r = 128 * wm + 32 * i + frow;
-            const int c = 64 * wn + 32 * j + 8 * rq + 4 * h;
-            f32x2 lo = {acc[i][j][4 * rq + 0] * alpha_f, acc[i][j][4 * rq + 1] * alpha_f};
-            f32x2 hi = {acc[i][j][4 * rq + 2] * alpha_f, acc[i][j][4 * rq + 3] * alpha_f};
-            uint2 v;
-            v.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
-            v.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2));
-            *reinterpret_cast<uint2*>(smem + r * kBf16Pitch + 2 * c) = v;
-          }
-      barrier();
-      // read q of wave w: row 2 (8 q + w) + lane / 32, 16-byte chunk lane % 32
-      u32x4 v[16];
-#pragma unroll
-      for (int q = 0; q < 16; ++q)
-        v[q] = *reinterpret_cast<const u32x4*>(smem + (2 * (8 * q + w) + h) * kBf16Pitch + 16 * frow);
-      __builtin_amdgcn_s_waitcnt(0xC07F);
-      barrier();
-      prologue_next();
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int64_t m = m0 + 2 * (8 * q + w) + h, nn = n0 + 8 * frow;
-        if (full || (m < M && nn < N))
-          __builtin_nontemporal_store(
-              v[q], reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(C) + m * ldc + nn));
-      }
-    } else {
-      // fp32: two passes of 128 rows (the waves with wm == p fill pass p)
+    int bf16_out = out_bf16, wme = wm;
+    asm volatile("" : "+s"(bf16_out), "+s"(wme));  // tested here, not held as masks
+    if (bf16_out) {
+      // two passes of 128 rows: the waves with wm == p write pass p
+      u32x4 v[2][8];
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
-        if (wm == p) {
+        if (wme == p) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -1261,31 +1301,84 @@ void gemm_mx_pp_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
 #pragma unroll
               for (int rq = 0; rq < 4; ++rq) {
                 const int r = 32 * i + frow;
-                const int c = 64 * wn + 32 * j + 8 * rq + 4 * h;
-                *reinterpret_cast<f32x4*>(smem + r * kF32Pitch + 4 * c) =
+                const int c = 64 * wn + 32 * j + 8 * rq + 4 * h;  // first of 4 bf16 columns
+                f32x2 lo = {acc[i][j][4 * rq + 0] * alpha_f, acc[i][j][4 * rq + 1] * alpha_f};
+                f32x2 hi = {acc[i][j][4 * rq + 2] * alpha_f, acc[i][j][4 * rq + 3] * alpha_f};
+                uint2 u;
+                u.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
+                u.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2));
+                *reinterpret_cast<uint2*>(stg + r * 512 + stage_chunk(r, c >> 3) + 8 * h) = u;
+              }
+        }
+        barrier();
+        // read q of wave w: row 16 q + 2 w + lane / 32, 16-byte chunk lane % 32
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int r = 16 * q + 2 * w + h;
+          v[p][q] = *reinterpret_cast<const u32x4*>(stg + r * 512 + stage_chunk(r, frow));
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        barrier();
+      }
+      step1_next();
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int64_t m = m0 + 128 * p + 16 * q + 2 * w + h, nn = n0 + 8 * frow;
+          if (full || (m < M && nn < N))
+            __builtin_nontemporal_store(
+                v[p][q], reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(C) + m * ldc + nn));
+        }
+      nst_prev = full ? 16 : 0;
+    } else {
+      // fp32: four passes of 64 rows (the waves with wm == p / 2 fill pass p with their
+      // accumulator rows 32 i, i = 2 (p % 2), 2 (p % 2) + 1); each pass stores as it goes
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        if (wme == (p >> 1)) {
+#pragma unroll
+          for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+              for (int rq = 0; rq < 4; ++rq) {
+                const int i = 2 * (p & 1) + ii;
+                const int r = 32 * ii + frow;
+                const int c = 64 * wn + 32 * j + 8 * rq + 4 * h;  // first of 4 fp32 columns
+                *reinterpret_cast<f32x4*>(stg + r * 1024 + stage_chunk(r, c >> 2)) =
                     f32x4{acc[i][j][4 * rq + 0] * alpha_f, acc[i][j][4 * rq + 1] * alpha_f,
                           acc[i][j][4 * rq + 2] * alpha_f, acc[i][j][4 * rq + 3] * alpha_f};
               }
         }
         barrier();
         // read q of wave w: row 8 q + w, 16-byte chunk lane
-        f32x4 v[16];
+        f32x4 v[8];
 #pragma unroll
-        for (int q = 0; q < 16; ++q)
-          v[q] = *reinterpret_cast<const f32x4*>(smem + (8 * q + w) * kF32Pitch + 16 * lane);
+        for (int q = 0; q < 8; ++q) {
+          const int r = 8 * q + w;
+          v[q] = *reinterpret_cast<const f32x4*>(stg + r * 1024 + stage_chunk(r, lane));
+        }
         __builtin_amdgcn_s_waitcnt(0xC07F);
         barrier();
-        if (p == 1) prologue_next();
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int64_t m = m0 + 128 * p + 8 * q + w, nn = n0 + 4 * lane;
+        for (int q = 0; q < 8; ++q) {
+          const int64_t m = m0 + 64 * p + 8 * q + w, nn = n0 + 4 * lane;
           if (full || (m < M && nn < N))
             __builtin_nontemporal_store(
                 v[q], reinterpret_cast<f32x4*>(reinterpret_cast<float*>(C) + m * ldc + nn));
         }
       }
+      step1_next();
+      nst_prev = 0;
     }
+    // the next tile starts once all but its step 1 (8 loads), the quarter of scale group 1
+    // (group 0's waves, one load) and these stores have landed
+    int gq = g, nq = n;
+    asm volatile("" : "+s"(gq), "+s"(nq));
+    in_flight = 8 + (gq == 0 && 4 < nq ? 1 : 0) + nst_prev;
   }
+
   wait_vmcnt<0>();  // no load may still be writing LDS when the workgroup ends
 }
 

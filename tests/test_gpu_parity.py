@@ -261,17 +261,22 @@ def test_gemm_hadamard_alpha(mx, orc):
     assert rel < 0.2
 
 
-@pytest.mark.parametrize("M,N,K", [(8096, 4064, 2048), (4352, 4352, 4096), (4384, 8224, 1024)])
-def test_gemm_chained_tiles(mx, orc, M, N, K):
+@pytest.mark.parametrize("M,N,K,out_dtype", [(8096, 4064, 2048, torch.bfloat16),
+                                               (4352, 4352, 4096, torch.bfloat16),
+                                               (4384, 8224, 1024, torch.bfloat16),
+                                               (4384, 4128, 3072, torch.float32),
+                                               (4608, 4352, 1024, torch.float32)])
+def test_gemm_chained_tiles(mx, orc, M, N, K, out_dtype):
     """More 256x256 tiles than compute units, so every workgroup of the resident grid walks
-    several tiles, with Hadamard + SR operands, bf16 output and whole 4-step scale groups.
-    Ragged M and N put partial tiles among them, and the columns of the output rows past N
-    must stay untouched."""
+    several tiles (each loading the next one's first steps while it finishes), with Hadamard +
+    SR operands, bf16 or fp32 output and whole 4-step scale groups (one, two, three or four per
+    tile). Ragged M and N put partial tiles among them, and the columns of the output rows past
+    N must stay untouched."""
     a = wl.student_t3((M, K), seed=31).to(DEV)
     b = wl.normal((N, K), 0.02, seed=32).to(DEV)
     (aq, as_), (bq, bs) = quantize_pair(mx, a, b, rule=1, rnd=1, had=1, mask=wl.sign_mask())
-    big = torch.full((M, N + 32), 7.0, dtype=torch.bfloat16, device=DEV)
-    out = mx.mx_gemm_fprop(aq, as_, 1, bq, bs, 1, out=big[:, :N], out_dtype=torch.bfloat16)
+    big = torch.full((M, N + 32), 7.0, dtype=out_dtype, device=DEV)
+    out = mx.mx_gemm_fprop(aq, as_, 1, bq, bs, 1, out=big[:, :N], out_dtype=out_dtype)
     torch.cuda.synchronize()
     rows = np.unique(np.concatenate([np.arange(0, M, 11), np.arange(M - 40, M)]))
     cols = np.arange(N)
