@@ -1019,8 +1019,8 @@ struct TileRes {
 __device__ __forceinline__ TileRes tile_res(const uint8_t* A, const uint8_t* As, int lga,
                                             const uint8_t* B, const uint8_t* Bs, int lgb,
                                             int64_t M, int64_t N, int64_t K, int64_t m0,
-                                            int64_t n0) {
-  const int64_t kbytes = K / 2, nkb = K / 32;
+                                            int64_t n0, int64_t kbytes) {
+  const int64_t nkb = K / 32;
   const int64_t rows_a = min((int64_t)256, M - m0), rows_b = min((int64_t)256, N - n0);
   TileRes r;
   r.ra = rsrc_words(A + m0 * kbytes, rows_a * kbytes);
@@ -1033,16 +1033,25 @@ __device__ __forceinline__ TileRes tile_res(const uint8_t* A, const uint8_t* As,
 }
 }  // namespace pp
 
+// AF, BF: operand formats as the matrix instruction numbers them (4 = E2M1; 0 = E4M3 and
+// 1 = E5M2 for MXFP8). A step is 128 code bytes of each row either way: 256 FP4 values in four
+// 64-k sub-steps, or 128 FP8 values in two. A scale group holds a row's 32 scale bytes of 4
+// FP4 steps (8 per step) or of 8 FP8 steps (4 per step).
+template <int AF, int BF>
 __global__ __launch_bounds__(pp::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_mx_pp_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, int lga,
                        const uint8_t* __restrict__ B, const uint8_t* __restrict__ Bs, int lgb,
                        int64_t M, int64_t N, int64_t K, float alpha_f, int out_bf16,
                        void* __restrict__ C, int64_t ldc, int nbm, int nbn) {
   using namespace pp;
+  constexpr bool F8 = AF != 4;
+  static_assert(F8 == (BF != 4), "both operands FP4 or both FP8");
+  constexpr int kSub = F8 ? 2 : 4;   // 64-k sub-steps per step
+  constexpr int kGS = F8 ? 8 : 4;    // steps per scale group
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kLds];
   const int nblocks = nbm * nbn;
-  const int64_t kbytes = K / 2, nkb = K / 32;
-  const int n = (int)(K / 256);  // steps per tile, a multiple of 4
+  const int64_t kbytes = F8 ? K : K / 2, nkb = K / 32;
+  const int n = (int)(kbytes / kRow);  // steps per tile, a multiple of 4
   __builtin_assume(n >= 4);
 
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -1082,7 +1091,7 @@ void gemm_mx_pp_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
     const int frow = lane & 31, h = lane >> 5;
     int64_t m0, n0;
     tile_origin(tile, nbm, nbn, m0, n0);
-    const TileRes R = tile_res(A, As, lga, B, Bs, lgb, M, N, K, m0, n0);
+    const TileRes R = tile_res(A, As, lga, B, Bs, lgb, M, N, K, m0, n0, kbytes);
 
     int voff0, goff_half;
     dma_lane_offsets(lane, voff0, goff_half);
@@ -1147,7 +1156,7 @@ void gemm_mx_pp_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
     };
     auto prologue1 = [&](const TileRes& r) {
       issue_codes(r, 1, g);
-      if (g == 0 && 4 < n) issue_quarter(r, 1, 0);
+      if (g == 0 && kGS < n) issue_quarter(r, 1, 0);
     };
     const bool first = tile == (int)blockIdx.x;
     if (first) {
@@ -1157,12 +1166,15 @@ void gemm_mx_pp_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
 
     // per-lane LDS offsets of the fragment and scale reads
     const int phi = (frow >> 1) & 7;
-    const int cb = (4 * h) ^ phi;  // chunk of sub-step s is cb ^ s
+    const int cb = (4 * h) ^ phi;  // chunk 4h + c of the row sits at cb ^ c
     const uint32_t a_row = (uint32_t)(128 * wm + frow) * kRow;
     const uint32_t b_row = kTile + (uint32_t)(64 * wn + frow) * kRow;
     const int sw = (frow >> 3) & 1;
-    const uint32_t sa_row = 2 * kStage + (uint32_t)(128 * wm + frow) * kGrpRow + 4 * h;
-    const uint32_t sb_row = 2 * kStage + kGrpOp + (uint32_t)(64 * wn + frow) * kGrpRow + 4 * h;
+    // FP4: the lane half's 4 scale bytes of a step are a word of their own; FP8: both halves
+    // read the step's word and the upper half shifts its two bytes down
+    const uint32_t sa_row = 2 * kStage + (uint32_t)(128 * wm + frow) * kGrpRow + (F8 ? 0 : 4 * h);
+    const uint32_t sb_row =
+        2 * kStage + kGrpOp + (uint32_t)(64 * wn + frow) * kGrpRow + (F8 ? 0 : 4 * h);
 
     v16f acc[4][2];
 #pragma unroll
@@ -1171,7 +1183,8 @@ void gemm_mx_pp_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-    u32x4 fa[4][4], fb[4][2];  // [sub-step][fragment]
+    using Frag = std::conditional_t<F8, u32x8, u32x4>;  // 32 values of a row per lane
+    Frag fa[kSub][4], fb[kSub][2];                      // [sub-step][fragment]
     uint32_t sa[4], sb[2];
 
     // memory phase of step k: fragments and scale words into registers (plus, in group 0, the
@@ -1179,18 +1192,30 @@ void gemm_mx_pp_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
     auto mem_phase = [&](int k, auto step0, auto grp) {
       constexpr int G = decltype(grp)::value;
       const uint8_t* st = smem + (k & 1) * kStage;
+      auto frag = [&](uint32_t row, int ss) {
+        if constexpr (F8) {
+          // the matrix instruction's 8-bit layout: lane half h holds values 16h .. 16h+15 of
+          // each of the sub-step's two k-blocks, i.e. chunks 4ss + h and 4ss + 2 + h
+          const uint32_t c = 16u * (uint32_t)((4 * ss + h) ^ phi);
+          const u32x4 lo = *reinterpret_cast<const u32x4*>(st + row + c);
+          const u32x4 hi = *reinterpret_cast<const u32x4*>(st + row + (c ^ 32u));
+          return Frag{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        } else {  // chunk 4h + ss
+          return *reinterpret_cast<const Frag*>(st + row + 16u * (uint32_t)(cb ^ ss));
+        }
+      };
 #pragma unroll
-      for (int ss = 0; ss < 4; ++ss) {
-        const uint32_t c = 16u * (uint32_t)(cb ^ ss);
+      for (int ss = 0; ss < kSub; ++ss) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          fa[ss][i] = *reinterpret_cast<const u32x4*>(st + a_row + 4096 * i + c);
+        for (int i = 0; i < 4; ++i) fa[ss][i] = frag(a_row + 4096 * i, ss);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          fb[ss][j] = *reinterpret_cast<const u32x4*>(st + b_row + 4096 * j + c);
+        for (int j = 0; j < 2; ++j) fb[ss][j] = frag(b_row + 4096 * j, ss);
       }
-      const int t4 = k & 3;
-      const uint32_t sofs = ((k >> 2) & 1) * kGrp + 16 * ((t4 >> 1) ^ sw) + 8 * (t4 & 1);
+      // step k's scale bytes: FP4 8 per row (word 4h + ...), FP8 4 per row
+      const int t = k & (kGS - 1);
+      const uint32_t sofs =
+          F8 ? ((k >> 3) & 1) * kGrp + 16 * ((t >> 2) ^ sw) + 4 * (t & 3)
+             : ((k >> 2) & 1) * kGrp + 16 * ((t >> 1) ^ sw) + 8 * (t & 1);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         sa[i] = *reinterpret_cast<const uint32_t*>(smem + sa_row + 1024 * i + sofs);
@@ -1199,9 +1224,20 @@ void gemm_mx_pp_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
         sb[j] = *reinterpret_cast<const uint32_t*>(smem + sb_row + 1024 * j + sofs);
       if (G == 0 && k >= 1 && k + 1 < n) {
         issue_codes(R, k + 1, 0);
-        if (k + 4 < n) issue_quarter(R, (k + 4) >> 2, (k + 4) & 3);  // groups of this tile only
+        // quarter p of scale group G' goes out at step kGS (G' - 1) + p (groups of this tile
+        // only)
+        const int v = k + kGS;
+        if ((v & (kGS - 1)) < 4 && (v & ~(kGS - 1)) < n) issue_quarter(R, v / kGS, v & (kGS - 1));
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage k are done
+      if constexpr (F8) {
+        // the scale of a sub-step's k-block b comes from lane half b: byte 2ss + h of the
+        // step's word, i.e. byte 2ss after a shift by one byte on the upper half
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sa[i] >>= 8 * h;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) sb[j] >>= 8 * h;
+      }
       if constexpr (G == 1) {
         // B of step k + 1 has landed (at k = 0 the previous tile's output stores, issued after
         // it, may still be in flight)
@@ -1212,14 +1248,15 @@ void gemm_mx_pp_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
     };
     auto compute_phase = [&]() {
       __builtin_amdgcn_s_setprio(1);
-      static_for<4>([&](auto ssc) {
+      static_for<kSub>([&](auto ssc) {
         constexpr int SS = decltype(ssc)::value;
+        constexpr int OP = F8 ? 2 * SS : SS;  // scale byte of the sub-step
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int j = 0; j < 2; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                as_operand(fb[SS][j]), as_operand(fa[SS][i]), acc[i][j], 4, 4, SS, sb[j], SS, sa[i]);
+                as_operand(fb[SS][j]), as_operand(fa[SS][i]), acc[i][j], BF, AF, OP, sb[j], OP, sa[i]);
       });
       __builtin_amdgcn_s_setprio(0);
     };
@@ -1270,7 +1307,7 @@ void gemm_mx_pp_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
     if (has_next) {
       int64_t nm0, nn0;
       tile_origin(next, nbm, nbn, nm0, nn0);
-      prologue0(tile_res(A, As, lga, B, Bs, lgb, M, N, K, nm0, nn0));
+      prologue0(tile_res(A, As, lga, B, Bs, lgb, M, N, K, nm0, nn0, kbytes));
     }
 
     // Epilogue: acc[i][j][r] = C[m][n], m = 128 wm + 32 i + (lane % 32),
@@ -1282,7 +1319,7 @@ void gemm_mx_pp_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
       if (has_next) {
         int64_t nm0, nn0;
         tile_origin(next, nbm, nbn, nm0, nn0);
-        prologue1(tile_res(A, As, lga, B, Bs, lgb, M, N, K, nm0, nn0));
+        prologue1(tile_res(A, As, lga, B, Bs, lgb, M, N, K, nm0, nn0, kbytes));
       }
     };
     const bool full = m0 + 256 <= M && n0 + 256 <= N;
@@ -1376,7 +1413,7 @@ void gemm_mx_pp_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
     // (group 0's waves, one load) and these stores have landed
     int gq = g, nq = n;
     asm volatile("" : "+s"(gq), "+s"(nq));
-    in_flight = 8 + (gq == 0 && 4 < nq ? 1 : 0) + nst_prev;
+    in_flight = 8 + (gq == 0 && kGS < nq ? 1 : 0) + nst_prev;
   }
 
   wait_vmcnt<0>();  // no load may still be writing LDS when the workgroup ends
@@ -1411,7 +1448,7 @@ hipError_t mx_launch_gemm(const GemmArgs& g) {
   constexpr int kS3 = kStreamWaves == 4 ? 8 : 4, kS0 = kStreamWaves == 4 ? 8 : 4;
   constexpr int kS1 = kStreamWaves == 4 ? 1 : 2;
   if (g.K % 1024 == 0 && g.K > 0)
-    hipLaunchKernelGGL(gemm_mx_pp_kernel, resident, dim3(pp::kThreads), 0, (hipStream_t)g.stream,
+    hipLaunchKernelGGL((gemm_mx_pp_kernel<4, 4>), resident, dim3(pp::kThreads), 0, (hipStream_t)g.stream,
                        g.a, g.as, lga, g.b, g.bs, lgb, g.M, g.N, g.K, alpha_f, g.out_bf16 ? 1 : 0,
                        g.c, g.ldc, (int)nbm, (int)nbn);
   else if (g.K % 512 == 0 && g.K > 0)
@@ -1463,6 +1500,16 @@ static hipError_t launch_gemm_fp8(const GemmArgs& g, const dim3 grid, float alph
   return hipGetLastError();
 }
 
+// MXFP8 with K a multiple of 512: the two-waves-per-SIMD kernel
+template <int AF, int BF>
+static hipError_t launch_gemm_fp8_pp(const GemmArgs& g, const dim3 grid, float alpha_f, int nbm,
+                                     int nbn) {
+  hipLaunchKernelGGL((gemm_mx_pp_kernel<AF, BF>), grid, dim3(pp::kThreads), 0,
+                     (hipStream_t)g.stream, g.a, g.as, 0, g.b, g.bs, 0, g.M, g.N, g.K, alpha_f,
+                     g.out_bf16 ? 1 : 0, g.c, g.ldc, nbm, nbn);
+  return hipGetLastError();
+}
+
 hipError_t mx_launch_gemm_fp8(const GemmArgs& g, int afmt, int bfmt) {
   const int64_t nbm = (g.M + kBM - 1) / kBM, nbn = (g.N + kBN - 1) / kBN;
   if (nbm * nbn > 0x7FFFFFFF) return hipErrorInvalidValue;
@@ -1471,6 +1518,14 @@ hipError_t mx_launch_gemm_fp8(const GemmArgs& g, int afmt, int bfmt) {
   const float alpha_f = __builtin_bit_cast(float, (uint32_t)(g.alpha + 127) << 23);
   const dim3 grid((unsigned)stream_grid(nbm * nbn));
   const int b = (afmt ? 2 : 0) | (bfmt ? 1 : 0);
+  if (g.K % 512 == 0) {
+    switch (b) {
+      case 0: return launch_gemm_fp8_pp<0, 0>(g, grid, alpha_f, (int)nbm, (int)nbn);
+      case 1: return launch_gemm_fp8_pp<0, 1>(g, grid, alpha_f, (int)nbm, (int)nbn);
+      case 2: return launch_gemm_fp8_pp<1, 0>(g, grid, alpha_f, (int)nbm, (int)nbn);
+      default: return launch_gemm_fp8_pp<1, 1>(g, grid, alpha_f, (int)nbm, (int)nbn);
+    }
+  }
   switch (b) {
     case 0: return launch_gemm_fp8<0, 0>(g, grid, alpha_f, 0, 0, (int)nbm, (int)nbn);
     case 1: return launch_gemm_fp8<0, 1>(g, grid, alpha_f, 0, 0, (int)nbm, (int)nbn);

@@ -119,6 +119,10 @@ GEMM_CASES = [
     (288, 320, 384),     # partial tiles in both dimensions, 3 k-stages
     (256, 512, 640),     # 5 k-stages: a partial scale group
     (544, 264 + 24, 1024),
+    # K a multiple of 512 (the two-waves-per-SIMD kernel, 128-k steps, 8-step scale groups)
+    (32, 32, 512),       # one partial tile, 4 steps: half a scale group
+    (288, 320, 1536),    # 12 steps: a whole and a half scale group, partial tiles
+    (544, 800, 2048),    # 3 x 4 tiles, 16 steps
 ]
 
 
@@ -139,6 +143,24 @@ def test_gemm_mxfp8_within_bound(mx, orc, M, N, K, afmt, bfmt, out_dtype):
     torch.cuda.synchronize()
     C, Cabs = orc.gemm_fp8(host(aq), host(as_), afmt, host(bq), host(bs), bfmt, M, N, K, -2)
     check_gemm(y, C, Cabs, rel=FP8_REL)
+
+
+@pytest.mark.parametrize("M,N,K,afmt,bfmt,out_dtype", [(4352, 4128, 1536, 1, 0, torch.float32),
+                                                      (4384, 4352, 4096, 0, 1, torch.bfloat16)])
+def test_gemm_mxfp8_chained_tiles(mx, orc, M, N, K, afmt, bfmt, out_dtype):
+    """More tiles than compute units, so every workgroup walks several, loading the next one's
+    first steps while it finishes; ragged M and N; the columns past N stay untouched."""
+    aq, as_, bq, bs = gemm_operands(mx, M, N, K, afmt, bfmt, seed=7)
+    big = torch.full((M, N + 32), 7.0, dtype=out_dtype, device=DEV)
+    out = mx.mx_gemm_mxfp8(aq, as_, afmt, bq, bs, bfmt, alpha_exp=-2, out=big[:, :N],
+                           out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, M, 13), np.arange(M - 40, M)]))
+    cols = np.arange(N)
+    C, Cabs = orc.gemm_fp8(host(aq[rows]), host(as_[rows]), afmt, host(bq), host(bs), bfmt,
+                           len(rows), N, K, -2)
+    check_gemm(out, C, Cabs, rows=rows, cols=cols, rel=FP8_REL)
+    assert torch.all(big[:, N:] == 7.0)
 
 
 def test_gemm_mxfp8_hadamard_alpha(mx, orc):
