@@ -1036,16 +1036,18 @@ __device__ __forceinline__ TileRes tile_res(const uint8_t* A, const uint8_t* As,
 // AF, BF: operand formats as the matrix instruction numbers them (4 = E2M1; 0 = E4M3 and
 // 1 = E5M2 for MXFP8). A step is 128 code bytes of each row either way: 256 FP4 values in four
 // 64-k sub-steps, or 128 FP8 values in two. A scale group holds a row's 32 scale bytes of 4
-// FP4 steps (8 per step) or of 8 FP8 steps (4 per step).
-template <int AF, int BF>
+// FP4 steps (8 per step) or of 8 FP8 steps (4 per step). QOUT: the output is quantized in the
+// epilogue (1x32 blocks along N, qo) instead of stored.
+template <int AF, int BF, bool QOUT = false>
 __global__ __launch_bounds__(pp::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_mx_pp_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, int lga,
                        const uint8_t* __restrict__ B, const uint8_t* __restrict__ Bs, int lgb,
                        int64_t M, int64_t N, int64_t K, float alpha_f, int out_bf16,
-                       void* __restrict__ C, int64_t ldc, int nbm, int nbn) {
+                       void* __restrict__ C, int64_t ldc, int nbm, int nbn, GemmQuantOut qo) {
   using namespace pp;
   constexpr bool F8 = AF != 4;
   static_assert(F8 == (BF != 4), "both operands FP4 or both FP8");
+  static_assert(!(F8 && QOUT), "the quantizing epilogue takes FP4 operands");
   constexpr int kSub = F8 ? 2 : 4;   // 64-k sub-steps per step
   constexpr int kGS = F8 ? 8 : 4;    // steps per scale group
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kLds];
@@ -1325,7 +1327,68 @@ void gemm_mx_pp_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
     const bool full = m0 + 256 <= M && n0 + 256 <= N;
     int bf16_out = out_bf16, wme = wm;
     asm volatile("" : "+s"(bf16_out), "+s"(wme));  // tested here, not held as masks
-    if (bf16_out) {
+    if constexpr (QOUT) {
+      // Quantized output [P1 paragraph 1: rotate, scale, round and pack the output tile before
+      // it is stored]: four passes of 64 rows of the fp32 tile (times 2^alpha) through stage 1,
+      // as the fp32 output does; then thread t takes the 32-column block t % 8 of pass row t / 8
+      // whole, as the row quantizer does (random-field index of C[m][n]: m * N + n)
+      const int t = 64 * w + lane;
+      const int rr = t >> 3, bc = t & 7;
+      // accumulator rows 32 i, i = 2 (p % 2) + 0, 1, of the waves with wm == p / 2 (the
+      // accumulator index must be a constant, so the pass loop dispatches on p % 2)
+      auto write_pass = [&](auto half) {
+        constexpr int P1 = decltype(half)::value;
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+              constexpr int kI0 = 2 * P1;
+              const int r = 32 * ii + frow;
+              const int c = 64 * wn + 32 * j + 8 * rq + 4 * h;
+              *reinterpret_cast<f32x4*>(stg + r * 1024 + stage_chunk(r, c >> 2)) =
+                  f32x4{acc[kI0 + ii][j][4 * rq + 0] * alpha_f, acc[kI0 + ii][j][4 * rq + 1] * alpha_f,
+                        acc[kI0 + ii][j][4 * rq + 2] * alpha_f, acc[kI0 + ii][j][4 * rq + 3] * alpha_f};
+            }
+      };
+#pragma unroll 1
+      for (int p = 0; p < 4; ++p) {
+        if (wme == (p >> 1)) {
+          if (p & 1) write_pass(std::integral_constant<int, 1>{});
+          else write_pass(std::integral_constant<int, 0>{});
+        }
+        barrier();
+        float x[32];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(stg + rr * 1024 + stage_chunk(rr, 8 * bc + c));
+          x[4 * c] = v.x; x[4 * c + 1] = v.y; x[4 * c + 2] = v.z; x[4 * c + 3] = v.w;
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        barrier();  // the next pass may write stage 1
+        const int64_t m = m0 + 64 * p + rr, nb = n0 + 32 * bc;
+        if (m < M && nb < N) {
+          if (qo.hadamard) {
+#pragma unroll
+            for (int j = 0; j < 32; ++j)
+              x[j] = __uint_as_float(__float_as_uint(x[j]) ^ (((qo.sign_mask >> j) & 1u) << 31));
+            mxd::hadamard32_inlane(x);
+          }
+          const int64_t e0 = m * N + nb;
+          uint32_t sb;
+          u32x4 code;
+          if (qo.sr) code = qo.ceil ? mxd::quant_block32<true, true>(x, qo.seed, (uint64_t)e0 >> 3, sb)
+                                    : mxd::quant_block32<true, false>(x, qo.seed, (uint64_t)e0 >> 3, sb);
+          else code = qo.ceil ? mxd::quant_block32<false, true>(x, qo.seed, (uint64_t)e0 >> 3, sb)
+                              : mxd::quant_block32<false, false>(x, qo.seed, (uint64_t)e0 >> 3, sb);
+          __builtin_nontemporal_store(code, reinterpret_cast<u32x4*>(qo.codes + e0 / 2));
+          qo.scales[e0 / 32] = (uint8_t)sb;
+        }
+      }
+      step1_next();
+      nst_prev = 0;
+    } else if (bf16_out) {
       // two passes of 128 rows: the waves with wm == p write pass p
       u32x4 v[2][8];
 #pragma unroll
@@ -1450,7 +1513,7 @@ hipError_t mx_launch_gemm(const GemmArgs& g) {
   if (g.K % 1024 == 0 && g.K > 0)
     hipLaunchKernelGGL((gemm_mx_pp_kernel<4, 4>), resident, dim3(pp::kThreads), 0, (hipStream_t)g.stream,
                        g.a, g.as, lga, g.b, g.bs, lgb, g.M, g.N, g.K, alpha_f, g.out_bf16 ? 1 : 0,
-                       g.c, g.ldc, (int)nbm, (int)nbn);
+                       g.c, g.ldc, (int)nbm, (int)nbn, GemmQuantOut{});
   else if (g.K % 512 == 0 && g.K > 0)
     hipLaunchKernelGGL((gemm_mx_stream_kernel<kStreamWaves, 4, 2, kS3, kS0, kS1>), resident,
                        dim3(64 * kStreamWaves), 0, (hipStream_t)g.stream, g.a,
@@ -1478,7 +1541,11 @@ hipError_t mx_launch_gemm_quant(const GemmArgs& g, const GemmQuantOut& q) {
   const dim3 resident((unsigned)stream_grid(nbm * nbn));
   constexpr int kS3 = kStreamWaves == 4 ? 8 : 4, kS0 = kStreamWaves == 4 ? 8 : 4;
   constexpr int kS1 = kStreamWaves == 4 ? 1 : 2;
-  if (g.K % 512 == 0)
+  if (g.K % 1024 == 0 && (reinterpret_cast<uintptr_t>(q.codes) & 15) == 0)
+    hipLaunchKernelGGL((gemm_mx_pp_kernel<4, 4, true>), resident, dim3(pp::kThreads), 0,
+                       (hipStream_t)g.stream, g.a, g.as, lga, g.b, g.bs, lgb, g.M, g.N, g.K,
+                       alpha_f, 0, nullptr, 0, (int)nbm, (int)nbn, q);
+  else if (g.K % 512 == 0)
     hipLaunchKernelGGL((gemm_mx_stream_kernel<kStreamWaves, 4, 2, kS3, kS0, kS1, true>), resident,
                        dim3(64 * kStreamWaves), 0, (hipStream_t)g.stream, g.a, g.as, lga, g.b,
                        g.bs, lgb, g.M, g.N, g.K, alpha_f, 0, nullptr, 0, (int)nbm, (int)nbn, q);
@@ -1506,7 +1573,7 @@ static hipError_t launch_gemm_fp8_pp(const GemmArgs& g, const dim3 grid, float a
                                      int nbn) {
   hipLaunchKernelGGL((gemm_mx_pp_kernel<AF, BF>), grid, dim3(pp::kThreads), 0,
                      (hipStream_t)g.stream, g.a, g.as, 0, g.b, g.bs, 0, g.M, g.N, g.K, alpha_f,
-                     g.out_bf16 ? 1 : 0, g.c, g.ldc, nbm, nbn);
+                     g.out_bf16 ? 1 : 0, g.c, g.ldc, nbm, nbn, GemmQuantOut{});
   return hipGetLastError();
 }
 

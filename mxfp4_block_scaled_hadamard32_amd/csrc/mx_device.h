@@ -267,6 +267,66 @@ __device__ __forceinline__ uint32_t quant_chunk8(float (&w)[8], int q, uint32_t 
 }
 
 // ---------------------------------------------------------------------------------------------
+// A whole 1x32 block in one lane [P1 paragraphs 1-2; P3 "Why FP4 ..."].
+// hadamard32_inlane: the 32-point transform, spans 1, 2, 4, 8, 16, each output one IEEE add or
+// subtract of the stage's two inputs (the random signs are applied before, by the caller).
+// quant_block32: block maximum, scale byte, v = x * 2^-e, rounding, packing (value j in nibble
+// j % 8 of word j / 8). g0 is the block's first chunk index for the random fields (source
+// element index of value 0, divided by 8). sb gets the scale byte; a block with a non-finite
+// maximum gets 0xFF and zero codes.
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ void hadamard32_inlane(float (&w)[32]) {
+#pragma unroll
+  for (int h = 1; h < 32; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if (i & h) continue;
+      const float a = w[i], c = w[i + h];
+      w[i] = a + c;
+      w[i + h] = a - c;
+    }
+  }
+}
+
+template <bool SR, bool CEIL>
+__device__ __forceinline__ u32x4 quant_block32(float (&w)[32], uint64_t seed, uint64_t g0,
+                                               uint32_t& sb) {
+  // block maximum of |x| as bits: the unsigned maximum of the raw bits is the largest negative
+  // value (if any), the signed maximum the largest positive one (if any); with the sign bits
+  // cleared the larger of the two is the largest magnitude, NaN and infinity included
+  uint32_t mu = __float_as_uint(w[0]);
+  int32_t mi = (int32_t)mu;
+#pragma unroll
+  for (int j = 1; j < 31; j += 2) {  // one three-input maximum per two values
+    mu = max(max(mu, __float_as_uint(w[j])), __float_as_uint(w[j + 1]));
+    mi = max(max(mi, (int32_t)__float_as_uint(w[j])), (int32_t)__float_as_uint(w[j + 1]));
+  }
+  mu = max(mu, __float_as_uint(w[31]));
+  mi = max(mi, (int32_t)__float_as_uint(w[31]));
+  sb = scale_byte<CEIL>(max(mu & 0x7FFFFFFFu, (uint32_t)mi & 0x7FFFFFFFu));
+  u32x4 out = {0u, 0u, 0u, 0u};
+  if (sb != 0xFFu) {
+    const float inv = inv_scale_from_byte(sb);
+#pragma unroll
+    for (int j = 0; j < 32; ++j) w[j] = w[j] * inv;
+    uint32_t o[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const float (&v8)[8] = *reinterpret_cast<const float(*)[8]>(w + 8 * d);
+      if (SR) {
+        uint32_t rw[8];
+        sr_rand8(g0 + d, seed, rw);
+        o[d] = sr_pack8(v8, rw);
+      } else {
+        o[d] = cvt_rne_pack8(v8);
+      }
+    }
+    out = u32x4{o[0], o[1], o[2], o[3]};
+  }
+  return out;
+}
+
+// ---------------------------------------------------------------------------------------------
 // in-lane transpose of an 8x8 matrix of nibbles: R[j] nibble k -> R[k] nibble j
 // (swap 4x4 quadrants, then 2x2 sub-blocks, then single nibbles)
 // ---------------------------------------------------------------------------------------------

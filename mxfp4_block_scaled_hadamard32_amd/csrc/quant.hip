@@ -144,54 +144,10 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
         w[j] = __uint_as_float(__float_as_uint(w[j]) ^ (((sign_mask >> j) & 1u) << 31));
     }
   }
-  // 32-point transform [P1 paragraph 2]: spans 1, 2, 4, 8, 16, each output one IEEE add or
-  // subtract of the stage's two inputs
-  if (HAD) {
-#pragma unroll
-    for (int h = 1; h < 32; h <<= 1) {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        if (i & h) continue;
-        const float a = w[i], c = w[i + h];
-        w[i] = a + c;
-        w[i + h] = a - c;
-      }
-    }
-  }
-  // block maximum of |x| as bits: the unsigned maximum of the raw bits is the largest negative
-  // value (if any), the signed maximum the largest positive one (if any); with the sign bits
-  // cleared the larger of the two is the largest magnitude, NaN and infinity included
-  uint32_t mu = __float_as_uint(w[0]);
-  int32_t mi = (int32_t)mu;
-#pragma unroll
-  for (int j = 1; j < 31; j += 2) {  // one three-input maximum per two values
-    mu = max(max(mu, __float_as_uint(w[j])), __float_as_uint(w[j + 1]));
-    mi = max(max(mi, (int32_t)__float_as_uint(w[j])), (int32_t)__float_as_uint(w[j + 1]));
-  }
-  mu = max(mu, __float_as_uint(w[31]));
-  mi = max(mi, (int32_t)__float_as_uint(w[31]));
-  const uint32_t m = max(mu & 0x7FFFFFFFu, (uint32_t)mi & 0x7FFFFFFFu);
-  const uint32_t sb = scale_byte<CEIL>(m);
-  u32x4 out = {0u, 0u, 0u, 0u};
-  if (sb != 0xFFu) {
-    const float inv = inv_scale_from_byte(sb);
-#pragma unroll
-    for (int j = 0; j < 32; ++j) w[j] = w[j] * inv;
-    uint32_t o[4];
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      float* c = w + 8 * d;
-      const float (&v8)[8] = *reinterpret_cast<const float(*)[8]>(c);
-      if (SR) {
-        uint32_t rw[8];
-        sr_rand8((uint64_t)(4 * b + d), seed, rw);
-        o[d] = sr_pack8(v8, rw);
-      } else {
-        o[d] = cvt_rne_pack8(v8);
-      }
-    }
-    out = u32x4{o[0], o[1], o[2], o[3]};
-  }
+  // 32-point transform [P1 paragraph 2], then the block's scale and codes
+  if (HAD) hadamard32_inlane(w);
+  uint32_t sb;
+  const u32x4 out = quant_block32<SR, CEIL>(w, seed, (uint64_t)(4 * b), sb);
   __builtin_nontemporal_store(out, codes + b);
   scales[b] = (uint8_t)sb;
 }

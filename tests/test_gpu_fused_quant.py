@@ -45,8 +45,14 @@ def outward_f32(lo, hi):
     return lo32, hi32
 
 
-def check_epilogue_quant(orc, codes, scales, C, Cabs, had, mask, rule, rnd, seed):
+def check_epilogue_quant(orc, codes, scales, C, Cabs, had, mask, rule, rnd, seed, rows=None):
+    """C, Cabs: the oracle's product on all rows, or on the output rows `rows` (then codes and
+    scales are the kernel's full outputs and are sliced to those rows)."""
     T, N = C.shape
+    if rows is not None:
+        sel = torch.as_tensor(rows, device=codes.device)
+        codes, scales = codes[sel], scales[sel]
+    row_of = np.arange(T) if rows is None else np.asarray(rows)
     nb = N // 32
     bound = GEMM_REL * Cabs
     Cb = C.reshape(T, nb, 32)
@@ -82,7 +88,7 @@ def check_epilogue_quant(orc, codes, scales, C, Cabs, had, mask, rule, rnd, seed
     unique = 0
     for t in range(T):
         for n in range(N):
-            r = orc.sr_field(seed, t * N + n) if rnd else 0
+            r = orc.sr_field(seed, int(row_of[t]) * N + n) if rnd else 0
             c_lo = orc.e2m1_encode(float(vlo[t, n]), rnd, r)
             c_hi = orc.e2m1_encode(float(vhi[t, n]), rnd, r)
             d = orc.e2m1_decode(int(got[t, n]))
@@ -114,10 +120,12 @@ def test_fprop_quant_epilogue(mx, orc, T, N, K, rule, rnd, had, mask):
     check_epilogue_quant(orc, codes, scales, C, Cabs, had, mask, rule, rnd, 77)
 
 
-def test_fprop_quant_matches_separate_quantize_where_exact(mx, orc):
+@pytest.mark.parametrize("K", [512, 1024])
+def test_fprop_quant_matches_separate_quantize_where_exact(mx, orc, K):
     """Small integers times power-of-two scales make every fp32 accumulation exact, so the fused
-    output must equal mx_quantize of mx_gemm_fprop's fp32 output byte for byte."""
-    T, N, K = 64, 256, 512
+    output must equal mx_quantize of mx_gemm_fprop's fp32 output byte for byte (both kernels:
+    128-k steps, and 256-k steps with two waves per SIMD)."""
+    T, N = 64, 256
     g = torch.Generator().manual_seed(5)
     x = torch.randint(-6, 7, (T, K), generator=g).float()
     w = torch.randint(-6, 7, (N, K), generator=g).float() * 0.5
@@ -130,6 +138,19 @@ def test_fprop_quant_matches_separate_quantize_where_exact(mx, orc):
         c2, s2 = mx.mx_quantize(y, scale_rule=rule, round=rnd, hadamard=had, sign_mask=mask,
                                 seed=9)
         assert torch.equal(s1, s2) and torch.equal(c1, c2)
+
+
+def test_fprop_quant_chained_tiles(mx, orc):
+    """More output tiles than compute units (each workgroup walks several), partial edge tiles,
+    Hadamard with random signs, ceil scale and stochastic rounding in the epilogue."""
+    T, N, K = 4352, 4128, 1024
+    xq, xs, wq, ws = operands(mx, T, N, K, seed=3)
+    codes, scales = mx.mx_gemm_fprop_quant(xq, xs, 1, wq, ws, 1, alpha_exp=-5, scale_rule=1,
+                                           round=1, hadamard=1, sign_mask=0x9E3779B9, seed=5)
+    torch.cuda.synchronize()
+    rows = np.array([0, 255, 256, 2049, 4100, T - 1])
+    C, Cabs = orc.gemm(host(xq), host(xs), 1, host(wq), host(ws), 1, T, N, K, -5, rows=rows)
+    check_epilogue_quant(orc, codes, scales, C, Cabs, 1, 0x9E3779B9, 1, 1, 5, rows=rows)
 
 
 def test_fprop_quant_rejects_ragged_k(mx):
