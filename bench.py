@@ -616,10 +616,10 @@ def write_traffic(fetch_csv: str, write_csv: str, workload: str):
 
     def gemm_launches(table):
         # the MXFP4 GEMM with plain output: the ping-pong kernel that serves reductions of a
-        # multiple of 1024 (all three of this workload), else the streaming kernel with template
-        # arguments ..., QOUT false, A and B formats 4 (not the quantizing epilogue or MXFP8);
-        # the step's launches come first
-        vals = [vs for name, vs in table.items() if "gemm_mx_pp_kernel" in name]
+        # multiple of 1024 (all three of this workload; template arguments A and B formats 4,
+        # QOUT false), else the streaming kernel with template arguments ..., QOUT false, A and
+        # B formats 4 (not the quantizing epilogue or MXFP8); the step's launches come first
+        vals = [vs for name, vs in table.items() if "gemm_mx_pp_kernel<4, 4, false>" in name]
         if not vals:
             vals = [vs for name, vs in table.items()
                     if re.search(r"gemm_mx\w*<[^>]*false, 4, 4>", name)]
@@ -728,7 +728,7 @@ def main():
             **launches,
         },
         "roofline": {
-            "kernel": "gemm_mx_pp_kernel (Wgrad launch)",
+            "kernel": "gemm_mx_pp_kernel<4, 4, false> (Wgrad launch)",
             "bound": "mfma",
             "achieved": round(wgrad_tflops, 2),
             "peak": PEAK_FP4_TFLOPS,

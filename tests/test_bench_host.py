@@ -19,7 +19,9 @@ GEMM = "(anonymous namespace)::gemm_mx_stream_kernel<4, 4, 2, 8, 8, 1, false, 4,
 QOUT = "(anonymous namespace)::gemm_mx_stream_kernel<4, 4, 2, 8, 8, 1, true, 4, 4>(args)"
 FP8 = "(anonymous namespace)::gemm_mx_stream_kernel<4, 4, 2, 16, 2, 0, false, 0, 0>(args)"
 QUANT = "(anonymous namespace)::quant_rows_kernel<true, true, true, true>(args)"
-PP = "(anonymous namespace)::gemm_mx_pp_kernel(unsigned char const*, int)"
+PP = "void (anonymous namespace)::gemm_mx_pp_kernel<4, 4, false>(unsigned char const*, int)"
+PP_FP8 = "void (anonymous namespace)::gemm_mx_pp_kernel<1, 0, false>(unsigned char const*, int)"
+PP_QOUT = "void (anonymous namespace)::gemm_mx_pp_kernel<4, 4, true>(unsigned char const*, int)"
 COPY = "__amd_rocclr_copyBuffer"
 FETCH_KIB = {"fprop": 1_400_000.0, "dgrad": 1_500_000.0, "wgrad": 1_450_000.0}
 
@@ -87,8 +89,10 @@ def test_counter_values_sums_instances_in_dispatch_order(tmp_path):
     assert vals[COPY] == pytest.approx([4.0])
 
 
-@pytest.mark.parametrize("kw", [{}, {"gemm": PP}, {"gemm": PP, "extra": (GEMM,) * 12}],
-                         ids=["stream", "pingpong", "pingpong_then_stream"])
+@pytest.mark.parametrize("kw", [{}, {"gemm": PP}, {"gemm": PP, "extra": (GEMM,) * 12},
+                                {"gemm": PP, "extra": (PP_FP8, PP_QOUT) * 6}],
+                         ids=["stream", "pingpong", "pingpong_then_stream",
+                              "pingpong_then_fp8_and_quantizing"])
 def test_write_traffic_record(tmp_path, record_path, monkeypatch, kw):
     # the ping-pong kernel's launches are the step's when present, whatever streaming-kernel
     # launches follow in the run
