@@ -18,10 +18,6 @@ MX_SCALE_FLOOR, MX_SCALE_CEIL = 0, 1
 MX_ROUND_RNE, MX_ROUND_SR = 0, 1
 MX_E4M3, MX_E5M2 = 0, 1
 
-EXPORTS = ["mx_quantize", "mx_quantize_2d", "mx_dequantize", "mx_gemm_fprop", "mx_gemm_dgrad",
-           "mx_gemm_wgrad", "mx_status_string", "mx_version"]
-
-
 class mx_quant_opts(ctypes.Structure):
     _fields_ = [("scale_rule", ctypes.c_int32), ("round", ctypes.c_int32),
                 ("hadamard", ctypes.c_int32), ("sign_mask", ctypes.c_uint32),
