@@ -212,14 +212,25 @@ __device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
 // Converter random words of source elements 8g .. 8g+7: rw[k] = (~r_k << 16) | 0xFFFF with r_k
 // field k (16 bits) of the Philox output at counter g (the low half of output word k / 2 for
 // even k, the high half for odd k).
-__device__ __forceinline__ void sr_rand8(uint64_t g, uint64_t seed, uint32_t (&rw)[8]) {
+// The complemented Philox words of chunk g: field k (value k of the chunk) is the half k % 2 of
+// word k / 2, complemented.
+__device__ __forceinline__ u32x4 sr_words(uint64_t g, uint64_t seed) {
   const uint4 w = philox4x32_10<true>((uint32_t)g, (uint32_t)(g >> 32), 0u, 0u, (uint32_t)seed,
                                       (uint32_t)(seed >> 32));
-  const uint32_t nw[4] = {w.x, ~w.y, w.z, ~w.w};  // words 0 and 2 come complemented
+  return u32x4{w.x, ~w.y, w.z, ~w.w};  // words 0 and 2 come complemented
+}
+
+// converter word of the field in the low / high half of a complemented word
+__device__ __forceinline__ uint32_t sr_word_lo(uint32_t nw) { return (nw << 16) | 0xFFFFu; }
+__device__ __forceinline__ uint32_t sr_word_hi(uint32_t nw) { return nw | 0xFFFFu; }
+
+__device__ __forceinline__ void sr_rand8(uint64_t g, uint64_t seed, uint32_t (&rw)[8]) {
+  const u32x4 v = sr_words(g, seed);
+  const uint32_t nw[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    rw[2 * i] = (nw[i] << 16) | 0xFFFFu;
-    rw[2 * i + 1] = nw[i] | 0xFFFFu;
+    rw[2 * i] = sr_word_lo(nw[i]);
+    rw[2 * i + 1] = sr_word_hi(nw[i]);
   }
 }
 
@@ -288,9 +299,10 @@ __device__ __forceinline__ void hadamard32_inlane(float (&w)[32]) {
   }
 }
 
-template <bool SR, bool CEIL>
-__device__ __forceinline__ u32x4 quant_block32(float (&w)[32], uint64_t seed, uint64_t g0,
-                                               uint32_t& sb) {
+// quant_block32_with takes the stochastic-rounding words from rw_of(d, rw), which fills the
+// converter words of values 8d .. 8d+7.
+template <bool SR, bool CEIL, class RW>
+__device__ __forceinline__ u32x4 quant_block32_with(float (&w)[32], RW&& rw_of, uint32_t& sb) {
   // block maximum of |x| as bits: the unsigned maximum of the raw bits is the largest negative
   // value (if any), the signed maximum the largest positive one (if any); with the sign bits
   // cleared the larger of the two is the largest magnitude, NaN and infinity included
@@ -315,7 +327,7 @@ __device__ __forceinline__ u32x4 quant_block32(float (&w)[32], uint64_t seed, ui
       const float (&v8)[8] = *reinterpret_cast<const float(*)[8]>(w + 8 * d);
       if (SR) {
         uint32_t rw[8];
-        sr_rand8(g0 + d, seed, rw);
+        rw_of(d, rw);
         o[d] = sr_pack8(v8, rw);
       } else {
         o[d] = cvt_rne_pack8(v8);
@@ -324,6 +336,13 @@ __device__ __forceinline__ u32x4 quant_block32(float (&w)[32], uint64_t seed, ui
     out = u32x4{o[0], o[1], o[2], o[3]};
   }
   return out;
+}
+
+template <bool SR, bool CEIL>
+__device__ __forceinline__ u32x4 quant_block32(float (&w)[32], uint64_t seed, uint64_t g0,
+                                               uint32_t& sb) {
+  return quant_block32_with<SR, CEIL>(
+      w, [&](int d, uint32_t (&rw)[8]) { sr_rand8(g0 + d, seed, rw); }, sb);
 }
 
 // ---------------------------------------------------------------------------------------------

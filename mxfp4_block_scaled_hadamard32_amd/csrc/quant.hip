@@ -238,6 +238,34 @@ constexpr int kColTileRows = 256, kColTileCols = 128;
 constexpr int kColHalves = kColTileCols / 128;
 constexpr int kCodeStride = 144;  // LDS bytes per column of the code tile (128 + 16 padding)
 
+// Store phase of a column tile (after a workgroup barrier): the codes of a column leave as one
+// 128-byte piece (8 lanes per column, 16 bytes = one row block each, so that one store
+// instruction writes the whole pieces of 8 columns); thread t writes the scale bytes of column t.
+__device__ __forceinline__ void col_tile_store(int tid, int64_t rows, int64_t cols, int64_t rb0,
+                                               int nrb, int64_t ctile0, const uint8_t* ctile,
+                                               const uint8_t* stile, uint8_t* __restrict__ codes_t,
+                                               uint8_t* __restrict__ scales_t) {
+  const int64_t rows2 = rows / 2;
+#pragma unroll
+  for (int round = 0; round < kColTileCols * 8 / kThreads; ++round) {
+    const int c = round * (kThreads / 8) + (tid >> 3), rbl = tid & 7;
+    if (ctile0 + c < cols && rbl < nrb)
+      __builtin_nontemporal_store(
+          *reinterpret_cast<const u32x4*>(ctile + c * kCodeStride + rbl * 16),
+          reinterpret_cast<u32x4*>(codes_t + (ctile0 + c) * rows2 + rb0 * 16 + rbl * 16));
+  }
+  for (int cs = tid; cs < kColTileCols; cs += kThreads) {
+    if (ctile0 + cs >= cols) break;
+    uint8_t* dst = scales_t + (ctile0 + cs) * (rows / 32) + rb0;
+    const uint8_t* src = stile + cs * 8;
+    if (nrb == 8 && ((reinterpret_cast<uintptr_t>(dst) & 7) == 0)) {
+      *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(src);
+    } else {
+      for (int i = 0; i < nrb; ++i) dst[i] = src[i];
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // 1x32 blocks down the columns (blocks along rows), output in the layout of the transpose:
 // codes_t [cols][rows/2], scales_t [cols][rows/32]. A workgroup owns 256 rows x 128 columns;
@@ -315,29 +343,117 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
     }
   }
   __syncthreads();
+  col_tile_store(threadIdx.x, rows, cols, rb0, nrb, ctile0, ctile, stile, codes_t, scales_t);
+}
 
-  // codes: 8 lanes per column, 16 bytes (one row block) each, so that one store instruction
-  // writes the whole 128-byte pieces of 8 columns
-  const int64_t rows2 = rows / 2;
+// ---------------------------------------------------------------------------------------------
+// 1x32 blocks down the columns with stochastic rounding (bf16 input): the same workgroup tiles,
+// passes and output staging as quant_cols_kernel, but each lane quantizes whole 32-row columns
+// in its registers, as the row kernel does (no lane exchanges in the transform, one scale per
+// lane and column). A lane still loads an 8x8 patch (rows 8q.., columns 8cg..) and computes the
+// Philox words of its 8 patch rows; both go through the wave's own LDS area, 16 rows x 128
+// columns of 16-bit values at a time (the random fields have the layout of the values they
+// round): the lanes with q < 2 write rows 0-15, every lane reads the dword of columns 8cg + 2q,
+// 8cg + 2q + 1 of those rows, then the same for rows 16-31. Chunk cg of area row r sits at
+// cg ^ 4 (r / 8), so that the patch writes (2 rows x 16 chunks) and the dword reads (one row)
+// both spread over all banks.
+// ---------------------------------------------------------------------------------------------
+constexpr int kXRowBytes = kColTileCols * 2;  // one row of the wave's exchange area
+
+__device__ __forceinline__ uint32_t xchg_offset(int r, int cg) {  // r: row of the area, 0..15
+  return (uint32_t)(r * kXRowBytes + 16 * (cg ^ (4 * ((r >> 3) & 1))));
+}
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Four waves per SIMD (at most 128 registers) run it 7-10% faster than three.
+template <bool HAD, bool CEIL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
+void quant_cols_sr_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, uint32_t sign_mask,
+    uint64_t seed, uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t, int64_t n_rt,
+    int64_t n_ct) {
+  __shared__ __attribute__((aligned(16))) uint8_t ctile[kColTileCols * kCodeStride];
+  __shared__ __attribute__((aligned(16))) uint8_t stile[kColTileCols * 8];
+  __shared__ __attribute__((aligned(16))) uint8_t xarea[4 * 16 * kXRowBytes];
+  int64_t rt, ct;
+  if (!col_tile_of(n_rt, n_ct, rt, ct)) return;  // uniform per workgroup
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int q = lane & 3, cg = lane >> 2;
+  const int64_t rb0 = rt * 8;
+  const int nrb = (int)min((int64_t)8, rows / 32 - rb0);
+  const int64_t ctile0 = ct * kColTileCols;
+  uint8_t* const xa = xarea + wave * 16 * kXRowBytes;
+
+#pragma unroll 1
+  for (int pass = 0; pass < 2; ++pass) {
+    const int rbl = pass * 4 + wave;
+    if (rbl >= nrb) break;  // uniform per wave (rbl grows with the pass)
+    const int64_t c0 = ctile0 + cg * 8;
+    const bool live = c0 < cols;  // a quad past the last column loads and stores nothing
+    const int64_t rb = rb0 + rbl;
+    const int64_t r0 = rb * 32 + 8 * q;
+    u32x4 raw[8];
 #pragma unroll
-  for (int round = 0; round < kColTileCols * 8 / kThreads; ++round) {
-    const int c = round * (kThreads / 8) + (threadIdx.x >> 3), rbl = threadIdx.x & 7;
-    if (ctile0 + c < cols && rbl < nrb)
-      __builtin_nontemporal_store(
-          *reinterpret_cast<const u32x4*>(ctile + c * kCodeStride + rbl * 16),
-          reinterpret_cast<u32x4*>(codes_t + (ctile0 + c) * rows2 + rb0 * 16 + rbl * 16));
-  }
-  // scales: thread t writes the nrb scale bytes of column t (+256 per round)
-  for (int cs = threadIdx.x; cs < kColTileCols; cs += kThreads) {
-    if (ctile0 + cs >= cols) break;
-    uint8_t* dst = scales_t + (ctile0 + cs) * (rows / 32) + rb0;
-    const uint8_t* src = stile + cs * 8;
-    if (nrb == 8 && ((reinterpret_cast<uintptr_t>(dst) & 7) == 0)) {
-      *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(src);
-    } else {
-      for (int i = 0; i < nrb; ++i) dst[i] = src[i];
+    for (int j = 0; j < 8; ++j)
+      raw[j] = live ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + (r0 + j) * ld + c0))
+                    : u32x4{0u, 0u, 0u, 0u};
+    // random words first (their VALU work overlaps the loads), then the values, each through
+    // the exchange area in two halves of 16 rows: in half hf the lanes with q / 2 == hf write
+    // their patch rows (area row 8 (q % 2) + j), and every lane reads rows 16 hf .. 16 hf + 15
+    u32x4 wd[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) wd[j] = sr_words((uint64_t)((r0 + j) * cols + c0) >> 3, seed);
+    uint32_t rnd[32], val[32];
+    auto exchange = [&](const u32x4 (&src)[8], uint32_t (&dst)[32]) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        if ((q >> 1) == hf) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            *reinterpret_cast<u32x4*>(xa + xchg_offset(8 * (q & 1) + j, cg)) = src[j];
+        }
+        wave_sync();
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          dst[16 * hf + r] = *reinterpret_cast<const uint32_t*>(xa + xchg_offset(r, cg) + 4 * q);
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): read before the area is written again
+        wave_sync();
+      }
+    };
+    exchange(wd, rnd);
+    exchange(raw, val);
+    // columns 8cg + 2q + e, e = 0 (low halves) and 1 (high halves)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      float w[32];
+#pragma unroll
+      for (int r = 0; r < 32; ++r) {
+        const uint32_t s = HAD ? ((sign_mask >> r) & 1u) << 31 : 0u;
+        w[r] = __uint_as_float(e ? (val[r] & 0xFFFF0000u) ^ s : (val[r] << 16) + s);
+      }
+      if (HAD) hadamard32_inlane(w);
+      uint32_t sb;
+      const u32x4 code = quant_block32_with<true, CEIL>(
+          w,
+          [&](int d, uint32_t (&rw)[8]) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+              rw[k] = e ? sr_word_hi(rnd[8 * d + k]) : sr_word_lo(rnd[8 * d + k]);
+          },
+          sb);
+      const int cl = cg * 8 + 2 * q + e;  // column within the tile
+      *reinterpret_cast<u32x4*>(ctile + cl * kCodeStride + rbl * 16) = code;
+      stile[cl * 8 + rbl] = (uint8_t)sb;
     }
   }
+  __syncthreads();
+  col_tile_store(threadIdx.x, rows, cols, rb0, nrb, ctile0, ctile, stile, codes_t, scales_t);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -868,9 +984,14 @@ hipError_t launch_cols(const QuantArgs& a) {
   int64_t n_rt, n_ct;
   const int64_t nblocks = col_tile_grid(a.rows, a.cols, n_rt, n_ct);
   if (nblocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((quant_cols_kernel<BF16, HAD, SR, CEIL>), dim3((unsigned)nblocks),
-                     dim3(kThreads), 0, (hipStream_t)a.stream, a.x, a.rows, a.cols, a.ld,
-                     a.sign_mask, a.seed, a.codes, a.scales, n_rt, n_ct);
+  if constexpr (BF16 && SR)
+    hipLaunchKernelGGL((quant_cols_sr_kernel<HAD, CEIL>), dim3((unsigned)nblocks), dim3(kThreads), 0,
+                       (hipStream_t)a.stream, reinterpret_cast<const uint16_t*>(a.x), a.rows,
+                       a.cols, a.ld, a.sign_mask, a.seed, a.codes, a.scales, n_rt, n_ct);
+  else
+    hipLaunchKernelGGL((quant_cols_kernel<BF16, HAD, SR, CEIL>), dim3((unsigned)nblocks),
+                       dim3(kThreads), 0, (hipStream_t)a.stream, a.x, a.rows, a.cols, a.ld,
+                       a.sign_mask, a.seed, a.codes, a.scales, n_rt, n_ct);
   return hipGetLastError();
 }
 
