@@ -82,6 +82,20 @@ def test_quantize_1d_bit_exact(mx, orc, rows, cols, axis, dtype, rule, rnd, had,
     assert_bytes_equal(c, rc, "codes")
 
 
+@pytest.mark.parametrize("rule,rnd,had,mask", [(1, 1, 1, 0x9E3779B9), (0, 0, 0, 0), (1, 0, 1, 0)])
+def test_quantize_rows_many_waves_ragged_last(mx, orc, rule, rnd, had, mask):
+    """Contiguous bf16 rows over more waves than the GPU holds at once (8192 x 64 blocks), the
+    last wave holding 4 blocks."""
+    x = special_input(4100, 4128, torch.bfloat16, seed=41)
+    assert (4100 * 4128 // 32) % 64 == 4 and 4100 * 4128 // 32 > 8192 * 64
+    c, s = mx.mx_quantize(x.to(DEV), axis=1, scale_rule=rule, round=rnd, hadamard=had,
+                          sign_mask=mask, seed=1234)
+    rc, rs = orc.quantize(hostx(x), axis=1, scale_rule=rule, round_mode=rnd, hadamard=had,
+                          sign_mask=mask, seed=1234, nthreads=8)
+    assert_bytes_equal(s, rs, "scales")
+    assert_bytes_equal(c, rc, "codes")
+
+
 @pytest.mark.parametrize("axis", [1, 0])
 def test_quantize_strided_rows(mx, orc, axis):
     """ld > cols: a column slice of a wider tensor."""
