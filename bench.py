@@ -637,13 +637,13 @@ def write_traffic(fetch_csv: str, write_csv: str, workload: str):
         got = sum(write_l[name]) / len(write_l[name]) * 1024.0 * wf
         if abs(got - out_bytes) > 0.08 * out_bytes:  # beyond C: register spill traffic
             raise SystemExit(f"{name}: launch writes {got:.3e} B, expected its bf16 output {out_bytes:.3e} B")
+    def command(counter, csv_path):  # the counter pass that wrote csv_path (its -d folder)
+        return (f"rocprofv3 --pmc {counter} --output-format csv -d {os.path.dirname(csv_path)} "
+                "-o run -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline "
+                "--step-only --with-variants --copy-calibration")
     rec = {"gemm_sha": sha(GEMM_SRC), "fetch_factor": ff, "write_factor": wf,
-           "command_fetch": ("rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch "
-                             "-o run -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline "
-                             "--step-only --with-variants --copy-calibration"),
-           "command_write": ("rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write "
-                             "-o run -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline "
-                             "--step-only --with-variants --copy-calibration")}
+           "command_fetch": command("FETCH_SIZE", fetch_csv),
+           "command_write": command("WRITE_SIZE", write_csv)}
     for name, (M, Nn, Kk) in shapes.items():
         fv = sum(fetch_l[name]) / len(fetch_l[name])
         wv = sum(write_l[name]) / len(write_l[name])
