@@ -5,7 +5,6 @@ The library is built in-tree, next to this file, so it travels with the source t
 import os
 import shutil
 import subprocess
-import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)

@@ -738,7 +738,7 @@ __global__ __launch_bounds__(kThreads) void quant_2d_var_kernel(
 // ---------------------------------------------------------------------------------------------
 template <bool BF16, bool CEIL>
 __global__ __launch_bounds__(kThreads) void mismatch_map_kernel(
-    const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, u32x2* __restrict__ map,
+    const void* __restrict__ x, int64_t cols, int64_t ld, u32x2* __restrict__ map,
     int64_t nunits, int64_t ncg) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t u = (int64_t)blockIdx.x * 4 + wave;
@@ -1048,8 +1048,7 @@ hipError_t launch_mismatch(const void* x, int64_t rows, int64_t cols, int64_t ld
   const int64_t nblocks = (nunits + 3) / 4;
   if (nblocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL((mismatch_map_kernel<BF16, CEIL>), dim3((unsigned)nblocks), dim3(kThreads), 0,
-                     (hipStream_t)stream, x, rows, cols, ld, reinterpret_cast<u32x2*>(map), nunits,
-                     ncg);
+                     (hipStream_t)stream, x, cols, ld, reinterpret_cast<u32x2*>(map), nunits, ncg);
   return hipGetLastError();
 }
 
