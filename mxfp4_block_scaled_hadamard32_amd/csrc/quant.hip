@@ -241,20 +241,21 @@ constexpr int kCodeStride = 144;  // LDS bytes per column of the code tile (128 
 // Store phase of a column tile (after a workgroup barrier): the codes of a column leave as one
 // 128-byte piece (8 lanes per column, 16 bytes = one row block each, so that one store
 // instruction writes the whole pieces of 8 columns); thread t writes the scale bytes of column t.
+template <int TC = kColTileCols>
 __device__ __forceinline__ void col_tile_store(int tid, int64_t rows, int64_t cols, int64_t rb0,
                                                int nrb, int64_t ctile0, const uint8_t* ctile,
                                                const uint8_t* stile, uint8_t* __restrict__ codes_t,
                                                uint8_t* __restrict__ scales_t) {
   const int64_t rows2 = rows / 2;
 #pragma unroll
-  for (int round = 0; round < kColTileCols * 8 / kThreads; ++round) {
+  for (int round = 0; round < TC * 8 / kThreads; ++round) {
     const int c = round * (kThreads / 8) + (tid >> 3), rbl = tid & 7;
     if (ctile0 + c < cols && rbl < nrb)
       __builtin_nontemporal_store(
           *reinterpret_cast<const u32x4*>(ctile + c * kCodeStride + rbl * 16),
           reinterpret_cast<u32x4*>(codes_t + (ctile0 + c) * rows2 + rb0 * 16 + rbl * 16));
   }
-  for (int cs = tid; cs < kColTileCols; cs += kThreads) {
+  for (int cs = tid; cs < TC; cs += kThreads) {
     if (ctile0 + cs >= cols) break;
     uint8_t* dst = scales_t + (ctile0 + cs) * (rows / 32) + rb0;
     const uint8_t* src = stile + cs * 8;
@@ -347,22 +348,24 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------
-// 1x32 blocks down the columns with stochastic rounding (bf16 input): the same workgroup tiles,
-// passes and output staging as quant_cols_kernel, but each lane quantizes whole 32-row columns
-// in its registers, as the row kernel does (no lane exchanges in the transform, one scale per
-// lane and column). A lane still loads an 8x8 patch (rows 8q.., columns 8cg..) and computes the
-// Philox words of its 8 patch rows; both go through the wave's own LDS area, 16 rows x 128
-// columns of 16-bit values at a time (the random fields have the layout of the values they
-// round): the lanes with q < 2 write rows 0-15, every lane reads the dword of columns 8cg + 2q,
-// 8cg + 2q + 1 of those rows, then the same for rows 16-31. Chunk cg of area row r sits at
-// cg ^ 4 (r / 8), so that the patch writes (2 rows x 16 chunks) and the dword reads (one row)
-// both spread over all banks.
+// 1x32 blocks down the columns with stochastic rounding (bf16 input), whole 32-row columns per
+// lane, as the row kernel quantizes them (no lane exchanges in the transform, one scale per lane).
+// A workgroup owns 256 rows x 64 columns; pass p of wave w takes row block 4p + w, and lane l
+// column l of the tile. Lane (q, cg) = (l / 8, l % 8) loads the 8 columns 8cg.. of rows
+// 4q..4q+3 (8 lanes: one 128-byte row) and computes the Philox words of the same chunk of rows
+// q, q + 8, q + 16, q + 24. The wave's own 4 KiB of LDS holds 32 rows of 128 bytes: first the
+// values, which each lane reads back as the 16-bit entries of its column, then the random
+// fields, stored with the layout of the values they round and read back the same way. Every
+// access of the area covers whole 128-byte rows (no bank conflicts). A lane keeps the codes and
+// scales of its two passes in registers; once all waves are done with their areas, the same
+// 16 KiB hold the code tile for the store phase. With at most 64 registers and 16 KiB per
+// workgroup, eight waves share a SIMD. Measured on a 16384x28672 tensor (Hadamard, ceil, SR):
+// 128-column tiles with two columns per lane (128 registers, four waves per SIMD) 286-291 us;
+// this kernel with the code tile beside the exchange areas (26 KiB, six waves) 264-266 us; as
+// it stands 259-266 us. Code bytes stored straight from the lanes (16 bytes per line per store)
+// were 20-30% slower.
 // ---------------------------------------------------------------------------------------------
-constexpr int kXRowBytes = kColTileCols * 2;  // one row of the wave's exchange area
-
-__device__ __forceinline__ uint32_t xchg_offset(int r, int cg) {  // r: row of the area, 0..15
-  return (uint32_t)(r * kXRowBytes + 16 * (cg ^ (4 * ((r >> 3) & 1))));
-}
+constexpr int kColSrTileCols = 64;
 
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -370,90 +373,92 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Four waves per SIMD (at most 128 registers) run it 7-10% faster than three.
 template <bool HAD, bool CEIL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HAD ? 8 : 7, 8)))
 void quant_cols_sr_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, uint32_t sign_mask,
     uint64_t seed, uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t, int64_t n_rt,
     int64_t n_ct) {
-  __shared__ __attribute__((aligned(16))) uint8_t ctile[kColTileCols * kCodeStride];
-  __shared__ __attribute__((aligned(16))) uint8_t stile[kColTileCols * 8];
-  __shared__ __attribute__((aligned(16))) uint8_t xarea[4 * 16 * kXRowBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t xarea[4 * 4096];
+  uint8_t* const ctile = xarea;                                 // after both passes
+  uint8_t* const stile = xarea + kColSrTileCols * kCodeStride;  // after both passes
+  u32x4 codes[2];
+  uint32_t sbv[2];
   int64_t rt, ct;
   if (!col_tile_of(n_rt, n_ct, rt, ct)) return;  // uniform per workgroup
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int q = lane & 3, cg = lane >> 2;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar registers
+  const int q = lane >> 3, cg = lane & 7;
   const int64_t rb0 = rt * 8;
   const int nrb = (int)min((int64_t)8, rows / 32 - rb0);
-  const int64_t ctile0 = ct * kColTileCols;
-  uint8_t* const xa = xarea + wave * 16 * kXRowBytes;
+  const int64_t ctile0 = ct * kColSrTileCols;
+  uint8_t* const xa = xarea + wave * 4096;
+  // Lane parts of the addresses, fixed over the passes: the element offset of row 4q, chunk cg
+  // from the row block's first row (a piece past the last column reads the tile's first piece
+  // instead; its values are never stored), and the counter offset of row q, chunk cg.
+  const int64_t xo = 4 * q * ld + (ctile0 + 8 * cg < cols ? 8 * cg : 0);
+  const int64_t go = q * (cols >> 3) + cg;
 
-#pragma unroll 1
+#pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     const int rbl = pass * 4 + wave;
     if (rbl >= nrb) break;  // uniform per wave (rbl grows with the pass)
-    const int64_t c0 = ctile0 + cg * 8;
-    const bool live = c0 < cols;  // a quad past the last column loads and stores nothing
     const int64_t rb = rb0 + rbl;
-    const int64_t r0 = rb * 32 + 8 * q;
-    u32x4 raw[8];
+    const uint16_t* xb = x + rb * 32 * ld + ctile0;
+    u32x4 raw[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      raw[j] = live ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + (r0 + j) * ld + c0))
-                    : u32x4{0u, 0u, 0u, 0u};
-    // random words first (their VALU work overlaps the loads), then the values, each through
-    // the exchange area in two halves of 16 rows: in half hf the lanes with q / 2 == hf write
-    // their patch rows (area row 8 (q % 2) + j), and every lane reads rows 16 hf .. 16 hf + 15
-    u32x4 wd[8];
+    for (int j = 0; j < 4; ++j)
+      raw[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xb + j * ld + xo));
+    const uint64_t gb = (uint64_t)rb * 4 * (uint64_t)cols + (uint64_t)(ctile0 >> 3);
+    u32x4 wd[4];  // complemented Philox words of chunk cg of rows q + 8m
 #pragma unroll
-    for (int j = 0; j < 8; ++j) wd[j] = sr_words((uint64_t)((r0 + j) * cols + c0) >> 3, seed);
-    uint32_t rnd[32], val[32];
-    auto exchange = [&](const u32x4 (&src)[8], uint32_t (&dst)[32]) {
+    for (int m = 0; m < 4; ++m) wd[m] = sr_words(gb + (uint64_t)m * cols + go, seed);
+    // values: area row r = 128 bytes, the 64 columns in order
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        if ((q >> 1) == hf) {
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(xa + (4 * q + j) * 128 + 16 * cg) = raw[j];
+    wave_sync();
+    uint32_t val[32];  // row r of column `lane`
 #pragma unroll
-          for (int j = 0; j < 8; ++j)
-            *reinterpret_cast<u32x4*>(xa + xchg_offset(8 * (q & 1) + j, cg)) = src[j];
-        }
-        wave_sync();
+    for (int r = 0; r < 32; ++r) val[r] = *reinterpret_cast<const uint16_t*>(xa + r * 128 + 2 * lane);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): read before the area is written again
+    wave_sync();
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          dst[16 * hf + r] = *reinterpret_cast<const uint32_t*>(xa + xchg_offset(r, cg) + 4 * q);
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): read before the area is written again
-        wave_sync();
-      }
-    };
-    exchange(wd, rnd);
-    exchange(raw, val);
-    // columns 8cg + 2q + e, e = 0 (low halves) and 1 (high halves)
+    for (int m = 0; m < 4; ++m) *reinterpret_cast<u32x4*>(xa + (q + 8 * m) * 128 + 16 * cg) = wd[m];
+    wave_sync();
+    uint32_t sm = sign_mask;
+    asm volatile("" : "+s"(sm));  // sign bits made per pass, not held across the loop
+    float w[32];
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      float w[32];
+    for (int r = 0; r < 32; ++r)  // widen and apply the sign in one shift-and-add
+      w[r] = __uint_as_float((val[r] << 16) + (HAD ? ((sm >> r) & 1u) << 31 : 0u));
+    if (HAD) hadamard32_inlane(w);
+    uint32_t sb;
+    const u32x4 code = quant_block32_with<true, CEIL>(
+        w,
+        [&](int d, uint32_t (&rw)[8]) {
 #pragma unroll
-      for (int r = 0; r < 32; ++r) {
-        const uint32_t s = HAD ? ((sign_mask >> r) & 1u) << 31 : 0u;
-        w[r] = __uint_as_float(e ? (val[r] & 0xFFFF0000u) ^ s : (val[r] << 16) + s);
-      }
-      if (HAD) hadamard32_inlane(w);
-      uint32_t sb;
-      const u32x4 code = quant_block32_with<true, CEIL>(
-          w,
-          [&](int d, uint32_t (&rw)[8]) {
+          for (int k = 0; k < 8; ++k)  // the field of row 8d + k in the high half
+            rw[k] = sr_word_lo(*reinterpret_cast<const uint16_t*>(xa + (8 * d + k) * 128 + 2 * lane));
+        },
+        sb);
+    codes[pass] = code;
+    sbv[pass] = sb;
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // fields read before the next pass writes the area
+    wave_sync();
+  }
+  __syncthreads();  // every wave is done with its area
 #pragma unroll
-            for (int k = 0; k < 8; ++k)
-              rw[k] = e ? sr_word_hi(rnd[8 * d + k]) : sr_word_lo(rnd[8 * d + k]);
-          },
-          sb);
-      const int cl = cg * 8 + 2 * q + e;  // column within the tile
-      *reinterpret_cast<u32x4*>(ctile + cl * kCodeStride + rbl * 16) = code;
-      stile[cl * 8 + rbl] = (uint8_t)sb;
+  for (int pass = 0; pass < 2; ++pass) {
+    const int rbl = pass * 4 + wave;
+    if (rbl < nrb) {
+      *reinterpret_cast<u32x4*>(ctile + lane * kCodeStride + rbl * 16) = codes[pass];
+      stile[lane * 8 + rbl] = (uint8_t)sbv[pass];
     }
   }
   __syncthreads();
-  col_tile_store(threadIdx.x, rows, cols, rb0, nrb, ctile0, ctile, stile, codes_t, scales_t);
+  col_tile_store<kColSrTileCols>(threadIdx.x, rows, cols, rb0, nrb, ctile0, ctile, stile, codes_t,
+                                 scales_t);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -972,9 +977,10 @@ hipError_t launch_rows(const QuantArgs& a) {
 }
 
 // Grid of the 256x128 column tiles: 64 workgroup ids per 8 (column tile, row group) units.
-inline int64_t col_tile_grid(int64_t rows, int64_t cols, int64_t& n_rt, int64_t& n_ct) {
+inline int64_t col_tile_grid(int64_t rows, int64_t cols, int64_t& n_rt, int64_t& n_ct,
+                             int64_t tile_cols = kColTileCols) {
   n_rt = (rows + kColTileRows - 1) / kColTileRows;
-  n_ct = (cols + kColTileCols - 1) / kColTileCols;
+  n_ct = (cols + tile_cols - 1) / tile_cols;
   const int64_t units = n_ct * ((n_rt + 7) / 8);
   return ((units + 7) / 8) * 64;
 }
@@ -982,16 +988,19 @@ inline int64_t col_tile_grid(int64_t rows, int64_t cols, int64_t& n_rt, int64_t&
 template <bool BF16, bool HAD, bool SR, bool CEIL>
 hipError_t launch_cols(const QuantArgs& a) {
   int64_t n_rt, n_ct;
+  if constexpr (BF16 && SR) {
+    const int64_t nblocks = col_tile_grid(a.rows, a.cols, n_rt, n_ct, kColSrTileCols);
+    if (nblocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((quant_cols_sr_kernel<HAD, CEIL>), dim3((unsigned)nblocks), dim3(kThreads),
+                       0, (hipStream_t)a.stream, reinterpret_cast<const uint16_t*>(a.x), a.rows,
+                       a.cols, a.ld, a.sign_mask, a.seed, a.codes, a.scales, n_rt, n_ct);
+    return hipGetLastError();
+  }
   const int64_t nblocks = col_tile_grid(a.rows, a.cols, n_rt, n_ct);
   if (nblocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  if constexpr (BF16 && SR)
-    hipLaunchKernelGGL((quant_cols_sr_kernel<HAD, CEIL>), dim3((unsigned)nblocks), dim3(kThreads), 0,
-                       (hipStream_t)a.stream, reinterpret_cast<const uint16_t*>(a.x), a.rows,
-                       a.cols, a.ld, a.sign_mask, a.seed, a.codes, a.scales, n_rt, n_ct);
-  else
-    hipLaunchKernelGGL((quant_cols_kernel<BF16, HAD, SR, CEIL>), dim3((unsigned)nblocks),
-                       dim3(kThreads), 0, (hipStream_t)a.stream, a.x, a.rows, a.cols, a.ld,
-                       a.sign_mask, a.seed, a.codes, a.scales, n_rt, n_ct);
+  hipLaunchKernelGGL((quant_cols_kernel<BF16, HAD, SR, CEIL>), dim3((unsigned)nblocks),
+                     dim3(kThreads), 0, (hipStream_t)a.stream, a.x, a.rows, a.cols, a.ld,
+                     a.sign_mask, a.seed, a.codes, a.scales, n_rt, n_ct);
   return hipGetLastError();
 }
 

@@ -122,6 +122,19 @@ def test_quantize_strided_rows_hadamard_sr(mx, orc, dtype):
     assert_bytes_equal(c, rc, "codes")
 
 
+@pytest.mark.parametrize("had,rule", [(1, 1), (0, 1), (1, 0)])
+def test_quantize_columns_sr_strided_ragged(mx, orc, had, rule):
+    """Stochastic rounding down the columns of a bf16 slice (ld > cols): 200 columns leave a
+    last 64-column tile of 8, and 288 rows a last 256-row tile of one row block."""
+    big = special_input(288, 360, torch.bfloat16, seed=9).to(DEV)
+    x = big[:, 40:240]
+    opts = dict(scale_rule=rule, hadamard=had, sign_mask=0x9E3779B9 if had else 0, seed=4321)
+    c, s = mx.mx_quantize(x, axis=0, round=1, **opts)
+    rc, rs = orc.quantize(hostx(x.contiguous()), axis=0, round_mode=1, **opts)
+    assert_bytes_equal(s, rs, "scales")
+    assert_bytes_equal(c, rc, "codes")
+
+
 @pytest.mark.parametrize("axis", [1, 0])
 @pytest.mark.parametrize("rnd", [0, 1])
 def test_hadamard_overflow_block(mx, orc, axis, rnd):
