@@ -269,7 +269,8 @@ __device__ __forceinline__ void col_tile_store(int tid, int64_t rows, int64_t co
 
 // ---------------------------------------------------------------------------------------------
 // 1x32 blocks down the columns (blocks along rows), output in the layout of the transpose:
-// codes_t [cols][rows/2], scales_t [cols][rows/32]. A workgroup owns 256 rows x 128 columns;
+// codes_t [cols][rows/2], scales_t [cols][rows/32]; the fp32-input path (bf16 input takes the
+// whole-column kernel further down). A workgroup owns 256 rows x 128 columns;
 // wave w handles row blocks w and w + 4 of the tile, lane = 4 * column-group + q. Each lane's
 // 8 codes of a column (one dword) go to an LDS tile first, so the global writes are whole
 // 128-byte column pieces.
@@ -348,13 +349,13 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------
-// 1x32 blocks down the columns with stochastic rounding (bf16 input), whole 32-row columns per
-// lane, as the row kernel quantizes them (no lane exchanges in the transform, one scale per lane).
-// A workgroup owns 256 rows x 64 columns; pass p of wave w takes row block 4p + w, and lane l
-// column l of the tile. Lane (q, cg) = (l / 8, l % 8) loads the 8 columns 8cg.. of rows
-// 4q..4q+3 (8 lanes: one 128-byte row) and computes the Philox words of the same chunk of rows
-// q, q + 8, q + 16, q + 24. The wave's own 4 KiB of LDS holds 32 rows of 128 bytes: first the
-// values, which each lane reads back as the 16-bit entries of its column, then the random
+// 1x32 blocks down the columns of a bf16 tensor, whole 32-row columns per lane, as the row kernel
+// quantizes them (no lane exchanges in the transform, one scale per lane). A workgroup owns 256
+// rows x 64 columns; pass p of wave w takes row block 4p + w, and lane l column l of the tile.
+// Lane (q, cg) = (l / 8, l % 8) loads the 8 columns 8cg.. of rows 4q..4q+3 (8 lanes: one
+// 128-byte row) and, for stochastic rounding, computes the Philox words of the same chunk of
+// rows q, q + 8, q + 16, q + 24. The wave's own 4 KiB of LDS holds 32 rows of 128 bytes: first
+// the values, which each lane reads back as the 16-bit entries of its column, then the random
 // fields, stored with the layout of the values they round and read back the same way. Every
 // access of the area covers whole 128-byte rows (no bank conflicts). A lane keeps the codes and
 // scales of its two passes in registers; once all waves are done with their areas, the same
@@ -363,9 +364,10 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
 // 128-column tiles with two columns per lane (128 registers, four waves per SIMD) 286-291 us;
 // this kernel with the code tile beside the exchange areas (26 KiB, six waves) 264-266 us; as
 // it stands 259-266 us. Code bytes stored straight from the lanes (16 bytes per line per store)
-// were 20-30% slower.
+// were 20-30% slower. With nearest-even rounding the 8192x14336 Hadamard case took 58.6 us with
+// the 8x8-patch kernel below and 54.8-55.4 us here.
 // ---------------------------------------------------------------------------------------------
-constexpr int kColSrTileCols = 64;
+constexpr int kColLaneTileCols = 64;
 
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -373,15 +375,15 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <bool HAD, bool CEIL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HAD ? 8 : 7, 8)))
-void quant_cols_sr_kernel(
+template <bool HAD, bool SR, bool CEIL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HAD || !SR ? 8 : 7, 8)))
+void quant_cols_bf16_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, uint32_t sign_mask,
     uint64_t seed, uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t, int64_t n_rt,
     int64_t n_ct) {
   __shared__ __attribute__((aligned(16))) uint8_t xarea[4 * 4096];
   uint8_t* const ctile = xarea;                                 // after both passes
-  uint8_t* const stile = xarea + kColSrTileCols * kCodeStride;  // after both passes
+  uint8_t* const stile = xarea + kColLaneTileCols * kCodeStride;  // after both passes
   u32x4 codes[2];
   uint32_t sbv[2];
   int64_t rt, ct;
@@ -392,7 +394,7 @@ void quant_cols_sr_kernel(
   const int q = lane >> 3, cg = lane & 7;
   const int64_t rb0 = rt * 8;
   const int nrb = (int)min((int64_t)8, rows / 32 - rb0);
-  const int64_t ctile0 = ct * kColSrTileCols;
+  const int64_t ctile0 = ct * kColLaneTileCols;
   uint8_t* const xa = xarea + wave * 4096;
   // Lane parts of the addresses, fixed over the passes: the element offset of row 4q, chunk cg
   // from the row block's first row (a piece past the last column reads the tile's first piece
@@ -412,8 +414,10 @@ void quant_cols_sr_kernel(
       raw[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xb + j * ld + xo));
     const uint64_t gb = (uint64_t)rb * 4 * (uint64_t)cols + (uint64_t)(ctile0 >> 3);
     u32x4 wd[4];  // complemented Philox words of chunk cg of rows q + 8m
+    if (SR) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) wd[m] = sr_words(gb + (uint64_t)m * cols + go, seed);
+      for (int m = 0; m < 4; ++m) wd[m] = sr_words(gb + (uint64_t)m * cols + go, seed);
+    }
     // values: area row r = 128 bytes, the 64 columns in order
 #pragma unroll
     for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(xa + (4 * q + j) * 128 + 16 * cg) = raw[j];
@@ -423,9 +427,12 @@ void quant_cols_sr_kernel(
     for (int r = 0; r < 32; ++r) val[r] = *reinterpret_cast<const uint16_t*>(xa + r * 128 + 2 * lane);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): read before the area is written again
     wave_sync();
+    if (SR) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) *reinterpret_cast<u32x4*>(xa + (q + 8 * m) * 128 + 16 * cg) = wd[m];
-    wave_sync();
+      for (int m = 0; m < 4; ++m)
+        *reinterpret_cast<u32x4*>(xa + (q + 8 * m) * 128 + 16 * cg) = wd[m];
+      wave_sync();
+    }
     uint32_t sm = sign_mask;
     asm volatile("" : "+s"(sm));  // sign bits made per pass, not held across the loop
     float w[32];
@@ -434,7 +441,7 @@ void quant_cols_sr_kernel(
       w[r] = __uint_as_float((val[r] << 16) + (HAD ? ((sm >> r) & 1u) << 31 : 0u));
     if (HAD) hadamard32_inlane(w);
     uint32_t sb;
-    const u32x4 code = quant_block32_with<true, CEIL>(
+    const u32x4 code = quant_block32_with<SR, CEIL>(
         w,
         [&](int d, uint32_t (&rw)[8]) {
 #pragma unroll
@@ -457,7 +464,7 @@ void quant_cols_sr_kernel(
     }
   }
   __syncthreads();
-  col_tile_store<kColSrTileCols>(threadIdx.x, rows, cols, rb0, nrb, ctile0, ctile, stile, codes_t,
+  col_tile_store<kColLaneTileCols>(threadIdx.x, rows, cols, rb0, nrb, ctile0, ctile, stile, codes_t,
                                  scales_t);
 }
 
@@ -988,19 +995,20 @@ inline int64_t col_tile_grid(int64_t rows, int64_t cols, int64_t& n_rt, int64_t&
 template <bool BF16, bool HAD, bool SR, bool CEIL>
 hipError_t launch_cols(const QuantArgs& a) {
   int64_t n_rt, n_ct;
-  if constexpr (BF16 && SR) {
-    const int64_t nblocks = col_tile_grid(a.rows, a.cols, n_rt, n_ct, kColSrTileCols);
+  if constexpr (BF16) {
+    const int64_t nblocks = col_tile_grid(a.rows, a.cols, n_rt, n_ct, kColLaneTileCols);
     if (nblocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((quant_cols_sr_kernel<HAD, CEIL>), dim3((unsigned)nblocks), dim3(kThreads),
-                       0, (hipStream_t)a.stream, reinterpret_cast<const uint16_t*>(a.x), a.rows,
-                       a.cols, a.ld, a.sign_mask, a.seed, a.codes, a.scales, n_rt, n_ct);
-    return hipGetLastError();
+    hipLaunchKernelGGL((quant_cols_bf16_kernel<HAD, SR, CEIL>), dim3((unsigned)nblocks),
+                       dim3(kThreads), 0, (hipStream_t)a.stream,
+                       reinterpret_cast<const uint16_t*>(a.x), a.rows, a.cols, a.ld, a.sign_mask,
+                       a.seed, a.codes, a.scales, n_rt, n_ct);
+  } else {
+    const int64_t nblocks = col_tile_grid(a.rows, a.cols, n_rt, n_ct);
+    if (nblocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((quant_cols_kernel<false, HAD, SR, CEIL>), dim3((unsigned)nblocks),
+                       dim3(kThreads), 0, (hipStream_t)a.stream, a.x, a.rows, a.cols, a.ld,
+                       a.sign_mask, a.seed, a.codes, a.scales, n_rt, n_ct);
   }
-  const int64_t nblocks = col_tile_grid(a.rows, a.cols, n_rt, n_ct);
-  if (nblocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((quant_cols_kernel<BF16, HAD, SR, CEIL>), dim3((unsigned)nblocks),
-                     dim3(kThreads), 0, (hipStream_t)a.stream, a.x, a.rows, a.cols, a.ld,
-                     a.sign_mask, a.seed, a.codes, a.scales, n_rt, n_ct);
   return hipGetLastError();
 }
 
