@@ -301,11 +301,10 @@ __device__ __forceinline__ void hadamard32_inlane(float (&w)[32]) {
 
 // quant_block32_with takes the stochastic-rounding words from rw_of(d, rw), which fills the
 // converter words of values 8d .. 8d+7.
-template <bool SR, bool CEIL, class RW>
-__device__ __forceinline__ u32x4 quant_block32_with(float (&w)[32], RW&& rw_of, uint32_t& sb) {
-  // block maximum of |x| as bits: the unsigned maximum of the raw bits is the largest negative
-  // value (if any), the signed maximum the largest positive one (if any); with the sign bits
-  // cleared the larger of the two is the largest magnitude, NaN and infinity included
+// Block maximum of |x| as bits: the unsigned maximum of the raw bits is the largest negative
+// value (if any), the signed maximum the largest positive one (if any); with the sign bits
+// cleared the larger of the two is the largest magnitude, NaN and infinity included.
+__device__ __forceinline__ uint32_t block32_amax_bits(const float (&w)[32]) {
   uint32_t mu = __float_as_uint(w[0]);
   int32_t mi = (int32_t)mu;
 #pragma unroll
@@ -315,7 +314,12 @@ __device__ __forceinline__ u32x4 quant_block32_with(float (&w)[32], RW&& rw_of, 
   }
   mu = max(mu, __float_as_uint(w[31]));
   mi = max(mi, (int32_t)__float_as_uint(w[31]));
-  sb = scale_byte<CEIL>(max(mu & 0x7FFFFFFFu, (uint32_t)mi & 0x7FFFFFFFu));
+  return max(mu & 0x7FFFFFFFu, (uint32_t)mi & 0x7FFFFFFFu);
+}
+
+template <bool SR, bool CEIL, class RW>
+__device__ __forceinline__ u32x4 quant_block32_with(float (&w)[32], RW&& rw_of, uint32_t& sb) {
+  sb = scale_byte<CEIL>(block32_amax_bits(w));
   u32x4 out = {0u, 0u, 0u, 0u};
   if (sb != 0xFFu) {
     const float inv = inv_scale_from_byte(sb);

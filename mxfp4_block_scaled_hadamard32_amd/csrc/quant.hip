@@ -832,6 +832,12 @@ __global__ __launch_bounds__(kThreads) void quant_rows_fp8_kernel(
 }
 
 constexpr int kCodeStride8 = 272;  // LDS bytes per column of the FP8 code tile (256 + 16)
+#ifndef COLS_FP8_LANE
+#define COLS_FP8_LANE 1
+#endif
+#ifndef COLS_FP8_WAVES
+#define COLS_FP8_WAVES 8
+#endif
 
 template <int FMT, bool BF16, bool HAD, bool SR, bool CEIL>
 __global__ __launch_bounds__(kThreads) void quant_cols_fp8_kernel(
@@ -913,6 +919,130 @@ __global__ __launch_bounds__(kThreads) void quant_cols_fp8_kernel(
     if (ctile0 + cs >= cols) break;
     uint8_t* dst = scales_t + (ctile0 + cs) * (rows / 32) + rb0;
     const uint8_t* src = stile + cs * 8;
+    if (nrb == 8 && ((reinterpret_cast<uintptr_t>(dst) & 7) == 0)) {
+      *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(src);
+    } else {
+      for (int i = 0; i < nrb; ++i) dst[i] = src[i];
+    }
+  }
+}
+
+// MXFP8 down the columns of a bf16 tensor with the whole-column kernel's layout: a workgroup
+// owns 256 rows x 64 columns, lane l the 32-row column l of a row block, whose 32 code bytes
+// (two 16-byte pieces) stay in registers over the two passes; after them the same LDS holds the
+// code tile (256 bytes per column, 272-byte stride) for 256-byte stores.
+template <int FMT, bool HAD, bool SR, bool CEIL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(COLS_FP8_WAVES, 8)))
+void quant_cols_fp8_bf16_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, uint32_t sign_mask,
+    uint64_t seed, uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t, int64_t n_rt,
+    int64_t n_ct) {
+  constexpr int kCodeBytes = kColLaneTileCols * kCodeStride8;  // 17 KiB
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kCodeBytes + kColLaneTileCols * 8];
+  uint8_t* const ctile = lds;               // after both passes
+  uint8_t* const stile = lds + kCodeBytes;  // after both passes
+  u32x4 codes[2][2];
+  uint32_t sbv[2];
+  int64_t rt, ct;
+  if (!col_tile_of(n_rt, n_ct, rt, ct)) return;  // uniform per workgroup
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar registers
+  const int q = lane >> 3, cg = lane & 7;
+  const int64_t rb0 = rt * 8;
+  const int nrb = (int)min((int64_t)8, rows / 32 - rb0);
+  const int64_t ctile0 = ct * kColLaneTileCols;
+  uint8_t* const xa = lds + wave * 4096;
+  const int64_t xo = 4 * q * ld + (ctile0 + 8 * cg < cols ? 8 * cg : 0);
+  const int64_t go = q * (cols >> 3) + cg;
+
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int rbl = pass * 4 + wave;
+    if (rbl >= nrb) break;  // uniform per wave (rbl grows with the pass)
+    const int64_t rb = rb0 + rbl;
+    const uint16_t* xb = x + rb * 32 * ld + ctile0;
+    u32x4 raw[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      raw[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xb + j * ld + xo));
+    const uint64_t gb = (uint64_t)rb * 4 * (uint64_t)cols + (uint64_t)(ctile0 >> 3);
+    u32x4 wd[4];  // complemented Philox words of chunk cg of rows q + 8m
+    if (SR) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) wd[m] = sr_words(gb + (uint64_t)m * cols + go, seed);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(xa + (4 * q + j) * 128 + 16 * cg) = raw[j];
+    wave_sync();
+    uint32_t val[32];  // row r of column `lane`
+#pragma unroll
+    for (int r = 0; r < 32; ++r) val[r] = *reinterpret_cast<const uint16_t*>(xa + r * 128 + 2 * lane);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): read before the area is written again
+    wave_sync();
+    if (SR) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        *reinterpret_cast<u32x4*>(xa + (q + 8 * m) * 128 + 16 * cg) = wd[m];
+      wave_sync();
+    }
+    uint32_t sm = sign_mask;
+    asm volatile("" : "+s"(sm));  // sign bits made per pass, not held across the loop
+    float w[32];
+#pragma unroll
+    for (int r = 0; r < 32; ++r)
+      w[r] = __uint_as_float((val[r] << 16) + (HAD ? ((sm >> r) & 1u) << 31 : 0u));
+    if (HAD) hadamard32_inlane(w);
+    const uint32_t sb = scale_byte_fp8<CEIL, FMT>(block32_amax_bits(w));
+    uint32_t o[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+    if (sb != 0xFFu) {
+      const float inv = inv_scale_from_byte(sb);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {  // rows 8d .. 8d + 7
+        float v8[8];
+        uint32_t r8[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          v8[k] = w[8 * d + k] * inv;
+          // the raw field of row 8d + k (the area holds it complemented)
+          r8[k] = SR ? ~(uint32_t)*reinterpret_cast<const uint16_t*>(xa + (8 * d + k) * 128 + 2 * lane)
+                     : 0u;
+        }
+        const uint2 pr = fp8_pack8<FMT, SR>(v8, r8);
+        o[2 * d] = pr.x;
+        o[2 * d + 1] = pr.y;
+      }
+    }
+    codes[pass][0] = u32x4{o[0], o[1], o[2], o[3]};
+    codes[pass][1] = u32x4{o[4], o[5], o[6], o[7]};
+    sbv[pass] = sb;
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // fields read before the next pass writes the area
+    wave_sync();
+  }
+  __syncthreads();  // every wave is done with its area
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int rbl = pass * 4 + wave;
+    if (rbl < nrb) {
+      *reinterpret_cast<u32x4*>(ctile + lane * kCodeStride8 + rbl * 32) = codes[pass][0];
+      *reinterpret_cast<u32x4*>(ctile + lane * kCodeStride8 + rbl * 32 + 16) = codes[pass][1];
+      stile[lane * 8 + rbl] = (uint8_t)sbv[pass];
+    }
+  }
+  __syncthreads();
+  // codes: 16 lanes per column, 16 bytes each (one store instruction writes the 256-byte pieces
+  // of 4 columns); then thread t the scale bytes of column t
+#pragma unroll
+  for (int round = 0; round < kColLaneTileCols * 16 / kThreads; ++round) {
+    const int c = round * (kThreads / 16) + (threadIdx.x >> 4), piece = threadIdx.x & 15;
+    if (ctile0 + c < cols && piece < 2 * nrb)
+      __builtin_nontemporal_store(
+          *reinterpret_cast<const u32x4*>(ctile + c * kCodeStride8 + 16 * piece),
+          reinterpret_cast<u32x4*>(codes_t + (ctile0 + c) * rows + rb0 * 32 + 16 * piece));
+  }
+  if ((int)threadIdx.x < kColLaneTileCols && ctile0 + threadIdx.x < cols) {
+    uint8_t* dst = scales_t + (ctile0 + threadIdx.x) * (rows / 32) + rb0;
+    const uint8_t* src = stile + threadIdx.x * 8;
     if (nrb == 8 && ((reinterpret_cast<uintptr_t>(dst) & 7) == 0)) {
       *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(src);
     } else {
@@ -1081,6 +1211,14 @@ hipError_t launch_fp8(const QuantArgs& a) {
                        dim3(kThreads), 0, (hipStream_t)a.stream, a.x, nchunks, cpr, a.ld,
                        a.ld == a.cols ? 1 : 0, a.sign_mask, a.seed,
                        reinterpret_cast<u32x2*>(a.codes), a.scales);
+  } else if (BF16 && COLS_FP8_LANE) {
+    int64_t n_rt, n_ct;
+    const int64_t nblocks = col_tile_grid(a.rows, a.cols, n_rt, n_ct, kColLaneTileCols);
+    if (nblocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((quant_cols_fp8_bf16_kernel<FMT, HAD, SR, CEIL>), dim3((unsigned)nblocks),
+                       dim3(kThreads), 0, (hipStream_t)a.stream,
+                       reinterpret_cast<const uint16_t*>(a.x), a.rows, a.cols, a.ld, a.sign_mask,
+                       a.seed, a.codes, a.scales, n_rt, n_ct);
   } else {
     int64_t n_rt, n_ct;
     const int64_t nblocks = col_tile_grid(a.rows, a.cols, n_rt, n_ct);
