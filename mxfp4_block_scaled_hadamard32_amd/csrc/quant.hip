@@ -241,21 +241,21 @@ constexpr int kCodeStride = 144;  // LDS bytes per column of the code tile (128 
 // Store phase of a column tile (after a workgroup barrier): the codes of a column leave as one
 // 128-byte piece (8 lanes per column, 16 bytes = one row block each, so that one store
 // instruction writes the whole pieces of 8 columns); thread t writes the scale bytes of column t.
-template <int TC = kColTileCols>
+template <int TC = kColTileCols, int NT = kThreads>
 __device__ __forceinline__ void col_tile_store(int tid, int64_t rows, int64_t cols, int64_t rb0,
                                                int nrb, int64_t ctile0, const uint8_t* ctile,
                                                const uint8_t* stile, uint8_t* __restrict__ codes_t,
                                                uint8_t* __restrict__ scales_t) {
   const int64_t rows2 = rows / 2;
 #pragma unroll
-  for (int round = 0; round < TC * 8 / kThreads; ++round) {
-    const int c = round * (kThreads / 8) + (tid >> 3), rbl = tid & 7;
+  for (int round = 0; round < TC * 8 / NT; ++round) {
+    const int c = round * (NT / 8) + (tid >> 3), rbl = tid & 7;
     if (ctile0 + c < cols && rbl < nrb)
       __builtin_nontemporal_store(
           *reinterpret_cast<const u32x4*>(ctile + c * kCodeStride + rbl * 16),
           reinterpret_cast<u32x4*>(codes_t + (ctile0 + c) * rows2 + rb0 * 16 + rbl * 16));
   }
-  for (int cs = tid; cs < TC; cs += kThreads) {
+  for (int cs = tid; cs < TC; cs += NT) {
     if (ctile0 + cs >= cols) break;
     uint8_t* dst = scales_t + (ctile0 + cs) * (rows / 32) + rb0;
     const uint8_t* src = stile + cs * 8;
@@ -351,16 +351,18 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
 // ---------------------------------------------------------------------------------------------
 // 1x32 blocks down the columns of a bf16 tensor, whole 32-row columns per lane, as the row kernel
 // quantizes them (no lane exchanges in the transform, one scale per lane). A workgroup owns 256
-// rows x 64 columns; pass p of wave w takes row block 4p + w, and lane l column l of the tile.
-// Lane (q, cg) = (l / 8, l % 8) loads the 8 columns 8cg.. of rows 4q..4q+3 (8 lanes: one
+// rows x 64 CWV columns, with 4 CWV waves: pass p of wave w takes row block 4p + w % 4 of the
+// 64 columns 64 (w / 4).., and lane l column l of those. Lane (q, cg) = (l / 8, l % 8) loads
+// the 8 columns 8cg.. of rows 4q..4q+3 (8 lanes: one
 // 128-byte row) and, for stochastic rounding, computes the Philox words of the same chunk of
 // rows q, q + 8, q + 16, q + 24. The wave's own 4 KiB of LDS holds 32 rows of 128 bytes: first
 // the values, which each lane reads back as the 16-bit entries of its column, then the random
 // fields, stored with the layout of the values they round and read back the same way. Every
 // access of the area covers whole 128-byte rows (no bank conflicts). A lane keeps the codes and
 // scales of its two passes in registers; once all waves are done with their areas, the same
-// 16 KiB hold the code tile for the store phase. With at most 64 registers and 16 KiB per
-// workgroup, eight waves share a SIMD. Measured on a 16384x28672 tensor (Hadamard, ceil, SR):
+// 16 CWV KiB hold the code tile for the store phase. With at most 64 registers and 16 KiB of
+// LDS per four waves, eight waves share a SIMD. Measured on a 16384x28672 tensor (Hadamard,
+// ceil, SR, CWV = 1):
 // 128-column tiles with two columns per lane (128 registers, four waves per SIMD) 286-291 us;
 // this kernel with the code tile beside the exchange areas (26 KiB, six waves) 264-266 us; as
 // it stands 259-266 us. Code bytes stored straight from the lanes (16 bytes per line per store)
@@ -375,15 +377,16 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <bool HAD, bool SR, bool CEIL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HAD || !SR ? 8 : 7, 8)))
+template <bool HAD, bool SR, bool CEIL, int CWV>
+__global__ __launch_bounds__(kThreads * CWV) __attribute__((amdgpu_waves_per_eu(HAD || !SR ? 8 : 7, 8)))
 void quant_cols_bf16_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, uint32_t sign_mask,
     uint64_t seed, uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t, int64_t n_rt,
     int64_t n_ct) {
-  __shared__ __attribute__((aligned(16))) uint8_t xarea[4 * 4096];
-  uint8_t* const ctile = xarea;                                 // after both passes
-  uint8_t* const stile = xarea + kColLaneTileCols * kCodeStride;  // after both passes
+  constexpr int TC = kColLaneTileCols * CWV;
+  __shared__ __attribute__((aligned(16))) uint8_t xarea[4 * CWV * 4096];
+  uint8_t* const ctile = xarea;                   // after both passes
+  uint8_t* const stile = xarea + TC * kCodeStride;  // after both passes
   u32x4 codes[2];
   uint32_t sbv[2];
   int64_t rt, ct;
@@ -391,28 +394,30 @@ void quant_cols_bf16_kernel(
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar registers
-  const int q = lane >> 3, cg = lane & 7;
+  const int q = lane >> 3, cg = lane & 7, wr = wave & 3, wc = wave >> 2;
   const int64_t rb0 = rt * 8;
   const int nrb = (int)min((int64_t)8, rows / 32 - rb0);
-  const int64_t ctile0 = ct * kColLaneTileCols;
+  const int64_t ctile0 = ct * TC;
+  // the wave's 64 columns; a half past the last column loads the tile's first half instead
+  const int64_t cw0 = ctile0 + 64 * wc, cl0 = cw0 < cols ? cw0 : ctile0;
   uint8_t* const xa = xarea + wave * 4096;
   // Lane parts of the addresses, fixed over the passes: the element offset of row 4q, chunk cg
   // from the row block's first row (a piece past the last column reads the tile's first piece
   // instead; its values are never stored), and the counter offset of row q, chunk cg.
-  const int64_t xo = 4 * q * ld + (ctile0 + 8 * cg < cols ? 8 * cg : 0);
+  const int64_t xo = 4 * q * ld + (cl0 + 8 * cg < cols ? 8 * cg : 0);
   const int64_t go = q * (cols >> 3) + cg;
 
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
-    const int rbl = pass * 4 + wave;
+    const int rbl = pass * 4 + wr;
     if (rbl >= nrb) break;  // uniform per wave (rbl grows with the pass)
     const int64_t rb = rb0 + rbl;
-    const uint16_t* xb = x + rb * 32 * ld + ctile0;
+    const uint16_t* xb = x + rb * 32 * ld + cl0;
     u32x4 raw[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       raw[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xb + j * ld + xo));
-    const uint64_t gb = (uint64_t)rb * 4 * (uint64_t)cols + (uint64_t)(ctile0 >> 3);
+    const uint64_t gb = (uint64_t)rb * 4 * (uint64_t)cols + (uint64_t)(cw0 >> 3);
     u32x4 wd[4];  // complemented Philox words of chunk cg of rows q + 8m
     if (SR) {
 #pragma unroll
@@ -457,15 +462,15 @@ void quant_cols_bf16_kernel(
   __syncthreads();  // every wave is done with its area
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
-    const int rbl = pass * 4 + wave;
+    const int rbl = pass * 4 + wr, cl = 64 * wc + lane;
     if (rbl < nrb) {
-      *reinterpret_cast<u32x4*>(ctile + lane * kCodeStride + rbl * 16) = codes[pass];
-      stile[lane * 8 + rbl] = (uint8_t)sbv[pass];
+      *reinterpret_cast<u32x4*>(ctile + cl * kCodeStride + rbl * 16) = codes[pass];
+      stile[cl * 8 + rbl] = (uint8_t)sbv[pass];
     }
   }
   __syncthreads();
-  col_tile_store<kColLaneTileCols>(threadIdx.x, rows, cols, rb0, nrb, ctile0, ctile, stile, codes_t,
-                                 scales_t);
+  col_tile_store<TC, kThreads * CWV>(threadIdx.x, rows, cols, rb0, nrb, ctile0, ctile, stile,
+                                      codes_t, scales_t);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -832,12 +837,6 @@ __global__ __launch_bounds__(kThreads) void quant_rows_fp8_kernel(
 }
 
 constexpr int kCodeStride8 = 272;  // LDS bytes per column of the FP8 code tile (256 + 16)
-#ifndef COLS_FP8_LANE
-#define COLS_FP8_LANE 1
-#endif
-#ifndef COLS_FP8_WAVES
-#define COLS_FP8_WAVES 8
-#endif
 
 template <int FMT, bool BF16, bool HAD, bool SR, bool CEIL>
 __global__ __launch_bounds__(kThreads) void quant_cols_fp8_kernel(
@@ -932,7 +931,7 @@ __global__ __launch_bounds__(kThreads) void quant_cols_fp8_kernel(
 // (two 16-byte pieces) stay in registers over the two passes; after them the same LDS holds the
 // code tile (256 bytes per column, 272-byte stride) for 256-byte stores.
 template <int FMT, bool HAD, bool SR, bool CEIL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(COLS_FP8_WAVES, 8)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
 void quant_cols_fp8_bf16_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, uint32_t sign_mask,
     uint64_t seed, uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t, int64_t n_rt,
@@ -1126,10 +1125,13 @@ template <bool BF16, bool HAD, bool SR, bool CEIL>
 hipError_t launch_cols(const QuantArgs& a) {
   int64_t n_rt, n_ct;
   if constexpr (BF16) {
-    const int64_t nblocks = col_tile_grid(a.rows, a.cols, n_rt, n_ct, kColLaneTileCols);
+    // nearest-even: 128-column tiles (two waves per row block) ran up to 6% faster than 64;
+    // stochastic rounding: 0.5-1% slower
+    constexpr int CWV = SR ? 1 : 2;
+    const int64_t nblocks = col_tile_grid(a.rows, a.cols, n_rt, n_ct, kColLaneTileCols * CWV);
     if (nblocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((quant_cols_bf16_kernel<HAD, SR, CEIL>), dim3((unsigned)nblocks),
-                       dim3(kThreads), 0, (hipStream_t)a.stream,
+    hipLaunchKernelGGL((quant_cols_bf16_kernel<HAD, SR, CEIL, CWV>), dim3((unsigned)nblocks),
+                       dim3(kThreads * CWV), 0, (hipStream_t)a.stream,
                        reinterpret_cast<const uint16_t*>(a.x), a.rows, a.cols, a.ld, a.sign_mask,
                        a.seed, a.codes, a.scales, n_rt, n_ct);
   } else {
@@ -1211,7 +1213,7 @@ hipError_t launch_fp8(const QuantArgs& a) {
                        dim3(kThreads), 0, (hipStream_t)a.stream, a.x, nchunks, cpr, a.ld,
                        a.ld == a.cols ? 1 : 0, a.sign_mask, a.seed,
                        reinterpret_cast<u32x2*>(a.codes), a.scales);
-  } else if (BF16 && COLS_FP8_LANE) {
+  } else if (BF16) {
     int64_t n_rt, n_ct;
     const int64_t nblocks = col_tile_grid(a.rows, a.cols, n_rt, n_ct, kColLaneTileCols);
     if (nblocks > 0x7FFFFFFF) return hipErrorInvalidValue;

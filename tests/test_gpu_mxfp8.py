@@ -61,6 +61,7 @@ QUANT_CASES = [
     (64, 96, 0, torch.bfloat16),
     (96, 136, 0, torch.float32),    # cols not a multiple of 128
     (544, 264, 0, torch.bfloat16),  # three 256-row tiles, the last partial
+    (288, 200, 0, torch.bfloat16),  # last 64-column tile of 8 columns, last row tile of one block
 ]
 OPTS = [
     # scale_rule, round, hadamard, sign_mask

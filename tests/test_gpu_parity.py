@@ -122,15 +122,17 @@ def test_quantize_strided_rows_hadamard_sr(mx, orc, dtype):
     assert_bytes_equal(c, rc, "codes")
 
 
+@pytest.mark.parametrize("rnd", [1, 0])
 @pytest.mark.parametrize("had,rule", [(1, 1), (0, 1), (1, 0)])
-def test_quantize_columns_sr_strided_ragged(mx, orc, had, rule):
-    """Stochastic rounding down the columns of a bf16 slice (ld > cols): 200 columns leave a
-    last 64-column tile of 8, and 288 rows a last 256-row tile of one row block."""
+def test_quantize_columns_strided_ragged(mx, orc, had, rule, rnd):
+    """Down the columns of a bf16 slice (ld > cols): 200 columns leave a last column tile of 8
+    (64-column tiles with SR, 128-column tiles with two waves per row block for nearest-even,
+    whose second half then has no columns), and 288 rows a last 256-row tile of one row block."""
     big = special_input(288, 360, torch.bfloat16, seed=9).to(DEV)
     x = big[:, 40:240]
     opts = dict(scale_rule=rule, hadamard=had, sign_mask=0x9E3779B9 if had else 0, seed=4321)
-    c, s = mx.mx_quantize(x, axis=0, round=1, **opts)
-    rc, rs = orc.quantize(hostx(x.contiguous()), axis=0, round_mode=1, **opts)
+    c, s = mx.mx_quantize(x, axis=0, round=rnd, **opts)
+    rc, rs = orc.quantize(hostx(x.contiguous()), axis=0, round_mode=rnd, **opts)
     assert_bytes_equal(s, rs, "scales")
     assert_bytes_equal(c, rc, "codes")
 
