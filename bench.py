@@ -57,6 +57,11 @@ def parse():
                         "layer), so that a profile of the run holds the step's launches alone")
     p.add_argument("--with-variants", action="store_true",
                    help="with --step-only, still run the MXFP8 and tile-size variant comparisons")
+    p.add_argument("--power", type=float, metavar="SECONDS",
+                   help="instead of the bench: run the Wgrad GEMM, the row and the column "
+                        "quantizer of the larger operand and the matrix-core probe back to back "
+                        "for SECONDS each while sampling board power and clock (amdsmi, "
+                        "read-only), and print one JSON record of them")
     p.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="no GPU work: turn the counter_collection.csv files of a FETCH_SIZE and "
                         "a WRITE_SIZE rocprofv3 pass over a --copy-calibration run into the "
@@ -494,6 +499,95 @@ def mfma_ceiling(torch, workgroups: int = 2048, iters: int = 1000, reps: int = 3
     return sorted(rates)[len(rates) // 2]
 
 
+def power_phases(layer, torch, secs: float):
+    """Board power, clock and hotspot temperature (amdsmi, read-only; sampled every 50 ms) while
+    each of the Wgrad GEMM, the row quantizer of X, the column quantizer of X and the
+    matrix-core probe runs back to back for `secs` seconds, after 1.5 s idle each. The first
+    third of each phase's samples (the ramp) is left out of its averages."""
+    import threading
+    try:
+        import amdsmi
+    except ImportError as e:
+        raise SystemExit(f"--power needs the amdsmi module: {e}")
+    import ctypes
+    from mxfp4_block_scaled_hadamard32_amd import build as hip_build
+    amdsmi.amdsmi_init()
+    h = amdsmi.amdsmi_get_processor_handles()[0]
+    try:
+        cap = amdsmi.amdsmi_get_power_cap_info(h)
+    except Exception as e:  # not every driver reports it
+        cap = {"error": str(e)}
+    samples, phase, stop = [], ["idle"], [False]
+
+    def sampler():
+        while not stop[0]:
+            try:
+                m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+                samples.append((phase[0], m.get("current_socket_power"), m.get("current_gfxclk"),
+                                m.get("temperature_hotspot")))
+            except Exception:
+                pass
+            time.sleep(0.05)
+
+    P = ctypes.CDLL(hip_build.PROBE_LIB)
+    P.mx_probe_mfma_fp4.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_uint32,
+                                    ctypes.c_void_p, ctypes.c_void_p]
+    P.mx_probe_mfma_fp4.restype = ctypes.c_int32
+    sink = torch.empty(2048 * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    b, mx = layer.buf, layer.mx
+
+    def wgrad():
+        mx.mx_gemm_wgrad(*b["dYt"], 1, *b["Xt"], 1, alpha_exp=layer.alpha["wgrad"], out=layer.dW)
+
+    def probe():
+        if P.mx_probe_mfma_fp4(2048, 1000, 0x9E3779B9, sink.data_ptr(), stream) != 0:
+            raise SystemExit("mx_probe_mfma_fp4 failed")
+
+    phases = [
+        ("wgrad_gemm", wgrad, layer.flops["wgrad"] / 1e12, "TFLOP/s"),
+        ("quant_Xq", lambda: layer.quant("Xq", layer.X, 1, layer.fprop_q, "X"),
+         layer.quant_bytes("Xq") / 1e9, "GB/s"),
+        ("quant_Xt", lambda: layer.quant("Xt", layer.X, 0, layer.wgrad_q, "X"),
+         layer.quant_bytes("Xt") / 1e9, "GB/s"),
+        ("mfma_probe", probe, 2048 * 4 * 1000 * 16 * 2.0 * 32 * 32 * 64 / 1e12, "TFLOP/s"),
+    ]
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    res = {"power_cap": cap, "seconds_per_phase": secs}
+    for name, fn, work, unit in phases:
+        phase[0] = "idle"
+        time.sleep(1.5)
+        fn()
+        torch.cuda.synchronize()
+        phase[0] = name
+        t0, n = time.perf_counter(), 0
+        while time.perf_counter() - t0 < secs:
+            for _ in range(4):
+                fn()
+            torch.cuda.synchronize()
+            n += 4
+        dt = time.perf_counter() - t0
+        phase[0] = "idle"
+        res[name] = {"launches": n, "us_per_launch": round(1e6 * dt / n, 1),
+                     "rate": round(work * n / dt, 1), "unit": unit}
+        print(f"bench: power phase {name} done ({n} launches)", file=sys.stderr, flush=True)
+    time.sleep(0.5)
+    stop[0] = True
+    th.join()
+    for name in ["idle"] + [ph[0] for ph in phases]:
+        v = [x for x in samples if x[0] == name]
+        tail = v if name == "idle" else v[len(v) // 3:]
+
+        def avg(i):
+            xs = [x[i] for x in tail if isinstance(x[i], (int, float)) and x[i] != 0xFFFF]
+            return round(sum(xs) / len(xs), 1) if xs else None
+        res.setdefault(name, {}).update({"samples": len(v), "socket_power_w": avg(1),
+                                         "gfxclk_mhz": avg(2), "hotspot_c": avg(3)})
+    amdsmi.amdsmi_shut_down()
+    return res
+
+
 def block_variants(mx, wl, torch, reps: int = 5):
     """Outside the timed step: the tile-size variants on the 2-D workload (W 14336x4096, X
     8192x4096, dY 8192x14336, bf16, ceil scale, RNE unless stated): 8x8, 32x32 and 64x64
@@ -675,6 +769,13 @@ def main():
     print(f"bench: generating {args.workload} inputs", file=sys.stderr, flush=True)
     layer = Layer(mx, wl, args.workload)
     torch.cuda.synchronize()
+    if args.power:
+        layer.step()
+        torch.cuda.synchronize()
+        rec = power_phases(layer, torch, args.power)
+        rec["workload"] = args.workload
+        print(json.dumps(rec), flush=True)
+        return
     if args.copy_calibration:
         a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
         a.fill_(1.0)
