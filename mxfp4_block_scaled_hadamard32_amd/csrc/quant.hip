@@ -384,6 +384,7 @@ void quant_cols_bf16_kernel(
     uint64_t seed, uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t, int64_t n_rt,
     int64_t n_ct) {
   constexpr int TC = kColLaneTileCols * CWV;
+  static_assert(TC * (kCodeStride + 8) <= 4 * CWV * 4096, "the code tile fits in the areas");
   __shared__ __attribute__((aligned(16))) uint8_t xarea[4 * CWV * 4096];
   uint8_t* const ctile = xarea;                   // after both passes
   uint8_t* const stile = xarea + TC * kCodeStride;  // after both passes
@@ -937,6 +938,7 @@ void quant_cols_fp8_bf16_kernel(
     uint64_t seed, uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t, int64_t n_rt,
     int64_t n_ct) {
   constexpr int kCodeBytes = kColLaneTileCols * kCodeStride8;  // 17 KiB
+  static_assert(kCodeBytes + kColLaneTileCols * 8 >= 4 * 4096, "the exchange areas fit");
   __shared__ __attribute__((aligned(16))) uint8_t lds[kCodeBytes + kColLaneTileCols * 8];
   uint8_t* const ctile = lds;               // after both passes
   uint8_t* const stile = lds + kCodeBytes;  // after both passes
