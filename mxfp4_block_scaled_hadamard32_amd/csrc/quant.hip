@@ -280,6 +280,7 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
     const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, uint32_t sign_mask,
     uint64_t seed, uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t, int64_t n_rt,
     int64_t n_ct) {
+  static_assert(!BF16, "bf16 input takes quant_cols_bf16_kernel");
   __shared__ __attribute__((aligned(16))) uint8_t ctile[kColTileCols * kCodeStride];
   __shared__ __attribute__((aligned(16))) uint8_t stile[kColTileCols * 8];
   int64_t rt, ct;
@@ -844,6 +845,7 @@ __global__ __launch_bounds__(kThreads) void quant_cols_fp8_kernel(
     const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, uint32_t sign_mask,
     uint64_t seed, uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t, int64_t n_rt,
     int64_t n_ct) {
+  static_assert(!BF16, "bf16 input takes quant_cols_fp8_bf16_kernel");
   __shared__ __attribute__((aligned(16))) uint8_t ctile[kColTileCols * kCodeStride8];
   __shared__ __attribute__((aligned(16))) uint8_t stile[kColTileCols * 8];
   int64_t rt, ct;
@@ -1215,7 +1217,7 @@ hipError_t launch_fp8(const QuantArgs& a) {
                        dim3(kThreads), 0, (hipStream_t)a.stream, a.x, nchunks, cpr, a.ld,
                        a.ld == a.cols ? 1 : 0, a.sign_mask, a.seed,
                        reinterpret_cast<u32x2*>(a.codes), a.scales);
-  } else if (BF16) {
+  } else if constexpr (BF16) {
     int64_t n_rt, n_ct;
     const int64_t nblocks = col_tile_grid(a.rows, a.cols, n_rt, n_ct, kColLaneTileCols);
     if (nblocks > 0x7FFFFFFF) return hipErrorInvalidValue;
@@ -1227,7 +1229,7 @@ hipError_t launch_fp8(const QuantArgs& a) {
     int64_t n_rt, n_ct;
     const int64_t nblocks = col_tile_grid(a.rows, a.cols, n_rt, n_ct);
     if (nblocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((quant_cols_fp8_kernel<FMT, BF16, HAD, SR, CEIL>), dim3((unsigned)nblocks),
+    hipLaunchKernelGGL((quant_cols_fp8_kernel<FMT, false, HAD, SR, CEIL>), dim3((unsigned)nblocks),
                        dim3(kThreads), 0, (hipStream_t)a.stream, a.x, a.rows, a.cols, a.ld,
                        a.sign_mask, a.seed, a.codes, a.scales, n_rt, n_ct);
   }
