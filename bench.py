@@ -178,6 +178,14 @@ class Layer:
         return res, ms
 
 
+def host_ahead(torch):
+    """Queues a few milliseconds of idle GPU work (a spin kernel) ahead of launches timed with
+    events, so that the host has queued them all before the GPU reaches them: kernels of 15-50 us
+    are otherwise timed together with the host's per-launch Python work. Called outside the
+    intervals the events measure."""
+    torch.cuda._sleep(5_000_000)
+
+
 def timed_steps(layer, torch, steps):
     """Runs `steps` steps with events around every launch; returns the events."""
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(layer.LAUNCHES) + 1)]
@@ -193,6 +201,7 @@ def llama8b_components(mx, wl, torch, steps: int = 5):
     layer = Layer(mx, wl, "llama8b_up")
     layer.step()
     torch.cuda.synchronize()
+    host_ahead(torch)
     evs = timed_steps(layer, torch, steps)
     torch.cuda.synchronize()
     res, _ = layer.launch_report(evs, prefix="llama8b_")
@@ -411,6 +420,7 @@ def mxfp8_attention(mx, wl, torch, reps: int = 5):
         fn()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
+        host_ahead(torch)
         e0.record()
         for _ in range(reps):
             fn()
@@ -604,6 +614,7 @@ def block_variants(mx, wl, torch, reps: int = 5):
         fn()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
+        host_ahead(torch)
         e0.record()
         for _ in range(reps):
             fn()
