@@ -159,20 +159,28 @@ __device__ __forceinline__ float sr_round_up23(float v) {
   return __builtin_copysignf(__builtin_ceilf(fabsf(v) * 8388608.0f), v);
 }
 
-// 8 scaled values -> 8 codes (value k in nibble k). Even values go to bytes 0-3 of one word and
-// odd values to bytes 0-3 of another, each code in the low nibble of its byte; the odd word is
-// then shifted into the high nibbles. rw[k] = (~r_k << 16) | 0xFFFF.
-__device__ __forceinline__ uint32_t sr_pack8(const float (&v)[8], const uint32_t (&rw)[8]) {
+// 8 values already rounded up by sr_round_up23 -> 8 codes (value k in nibble k). Even values go
+// to bytes 0-3 of one word and odd values to bytes 0-3 of another, each code in the low nibble
+// of its byte; the odd word is then shifted into the high nibbles. rw[k] = (~r_k << 16) | 0xFFFF.
+__device__ __forceinline__ uint32_t sr_pack8_up(const float (&up)[8], const uint32_t (&rw)[8]) {
   uint32_t ev, od;
-  cvt_sr_fp4_byte<0>(ev, sr_round_up23(v[0]), rw[0]);
-  cvt_sr_fp4_byte<0>(od, sr_round_up23(v[1]), rw[1]);
-  cvt_sr_fp4_byte<1>(ev, sr_round_up23(v[2]), rw[2]);
-  cvt_sr_fp4_byte<1>(od, sr_round_up23(v[3]), rw[3]);
-  cvt_sr_fp4_byte<2>(ev, sr_round_up23(v[4]), rw[4]);
-  cvt_sr_fp4_byte<2>(od, sr_round_up23(v[5]), rw[5]);
-  cvt_sr_fp4_byte<3>(ev, sr_round_up23(v[6]), rw[6]);
-  cvt_sr_fp4_byte<3>(od, sr_round_up23(v[7]), rw[7]);
+  cvt_sr_fp4_byte<0>(ev, up[0], rw[0]);
+  cvt_sr_fp4_byte<0>(od, up[1], rw[1]);
+  cvt_sr_fp4_byte<1>(ev, up[2], rw[2]);
+  cvt_sr_fp4_byte<1>(od, up[3], rw[3]);
+  cvt_sr_fp4_byte<2>(ev, up[4], rw[4]);
+  cvt_sr_fp4_byte<2>(od, up[5], rw[5]);
+  cvt_sr_fp4_byte<3>(ev, up[6], rw[6]);
+  cvt_sr_fp4_byte<3>(od, up[7], rw[7]);
   return ev | (od << 4);
+}
+
+// 8 scaled values -> 8 codes
+__device__ __forceinline__ uint32_t sr_pack8(const float (&v)[8], const uint32_t (&rw)[8]) {
+  float up[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) up[k] = sr_round_up23(v[k]);
+  return sr_pack8_up(up, rw);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -317,11 +325,31 @@ __device__ __forceinline__ uint32_t block32_amax_bits(const float (&w)[32]) {
   return max(mu & 0x7FFFFFFFu, (uint32_t)mi & 0x7FFFFFFFu);
 }
 
-template <bool SR, bool CEIL, class RW>
+// FOLD (stochastic rounding of values derived from bf16 input): |x| 2^-e 2^23 is one multiply.
+// It equals |v| 2^23 for v = fl32(x 2^-e) except where that product underflows to zero
+// (|x 2^-e| <= 2^-150), which the fold would round up on a zero field. A nonzero value derived
+// from bf16 by the transform's adds and subtracts is a multiple of 2^-133 (the smallest bf16),
+// so with e <= 16 the product is at least 2^-149; e > 16, and e < -104 (where 2^(23 - e)
+// overflows), take the two multiplies.
+template <bool SR, bool CEIL, bool FOLD = false, class RW>
 __device__ __forceinline__ u32x4 quant_block32_with(float (&w)[32], RW&& rw_of, uint32_t& sb) {
   sb = scale_byte<CEIL>(block32_amax_bits(w));
   u32x4 out = {0u, 0u, 0u, 0u};
-  if (sb != 0xFFu) {
+  if (SR && FOLD && sb - 23u <= 143u - 23u) {  // e = sb - 127 in [-104, 16]
+    const float inv23 = __uint_as_float((277u - sb) << 23);  // 2^(23 - e)
+    uint32_t o[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      float up[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        up[k] = __builtin_copysignf(__builtin_ceilf(fabsf(w[8 * d + k]) * inv23), w[8 * d + k]);
+      uint32_t rw[8];
+      rw_of(d, rw);
+      o[d] = sr_pack8_up(up, rw);
+    }
+    out = u32x4{o[0], o[1], o[2], o[3]};
+  } else if (sb != 0xFFu) {
     const float inv = inv_scale_from_byte(sb);
 #pragma unroll
     for (int j = 0; j < 32; ++j) w[j] = w[j] * inv;
@@ -342,10 +370,10 @@ __device__ __forceinline__ u32x4 quant_block32_with(float (&w)[32], RW&& rw_of, 
   return out;
 }
 
-template <bool SR, bool CEIL>
+template <bool SR, bool CEIL, bool FOLD = false>
 __device__ __forceinline__ u32x4 quant_block32(float (&w)[32], uint64_t seed, uint64_t g0,
                                                uint32_t& sb) {
-  return quant_block32_with<SR, CEIL>(
+  return quant_block32_with<SR, CEIL, FOLD>(
       w, [&](int d, uint32_t (&rw)[8]) { sr_rand8(g0 + d, seed, rw); }, sb);
 }
 

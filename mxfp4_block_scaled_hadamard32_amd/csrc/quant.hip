@@ -147,7 +147,7 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
   // 32-point transform [P1 paragraph 2], then the block's scale and codes
   if (HAD) hadamard32_inlane(w);
   uint32_t sb;
-  const u32x4 out = quant_block32<SR, CEIL>(w, seed, (uint64_t)(4 * b), sb);
+  const u32x4 out = quant_block32<SR, CEIL, BF16>(w, seed, (uint64_t)(4 * b), sb);
   __builtin_nontemporal_store(out, codes + b);
   scales[b] = (uint8_t)sb;
 }
@@ -448,7 +448,7 @@ void quant_cols_bf16_kernel(
       w[r] = __uint_as_float((val[r] << 16) + (HAD ? ((sm >> r) & 1u) << 31 : 0u));
     if (HAD) hadamard32_inlane(w);
     uint32_t sb;
-    const u32x4 code = quant_block32_with<SR, CEIL>(
+    const u32x4 code = quant_block32_with<SR, CEIL, true>(
         w,
         [&](int d, uint32_t (&rw)[8]) {
 #pragma unroll

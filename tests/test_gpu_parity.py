@@ -137,6 +137,49 @@ def test_quantize_columns_strided_ragged(mx, orc, had, rule, rnd):
     assert_bytes_equal(c, rc, "codes")
 
 
+def fold_boundary_blocks(nblk, had, seed):
+    """nblk 32-element blocks (one per row of the result) whose scale exponents straddle the
+    bounds of the SR kernels' folded scaling (e in [-104, 16]), with bf16 subnormal elements.
+    Without the transform: [M, t1 .. t31], M = 2^k or 1.5 2^k, t_j in {0, +-2^-133, +-2^-132,
+    +-3 2^-133}. With it (no random signs): [A, A, s2 .. s31], whose odd outputs are exactly the
+    transform of the small part (multiples of 2^-133, some of them +-2^-133) and even outputs
+    2A. Half of the blocks sit at e = 14 .. 19, the rest from e = -110 to 21."""
+    g = torch.Generator().manual_seed(seed)
+    k = torch.randint(-108, 24, (nblk,), generator=g)
+    near = torch.rand(nblk, generator=g) < 0.5
+    k = torch.where(near, torch.randint(16, 22, (nblk,), generator=g), k)
+    m = torch.where(torch.rand(nblk, generator=g) < 0.5, 1.0, 1.5) * torch.pow(2.0, k.double())
+    tiny = torch.tensor([0.0, 2.0 ** -133, -2.0 ** -133, 2.0 ** -132, -2.0 ** -132,
+                         3 * 2.0 ** -133, -3 * 2.0 ** -133], dtype=torch.float64)
+    small = tiny[torch.randint(0, len(tiny), (nblk, 32), generator=g)]
+    if had:
+        small[:, :2] = 0.0
+        small[:, 0] = m
+        small[:, 1] = m
+    else:
+        small[:, 0] = m
+    return small.to(torch.float32).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("axis", [1, 0])
+@pytest.mark.parametrize("had", [0, 1])
+@pytest.mark.parametrize("rule", [0, 1])
+def test_sr_scale_fold_boundaries(mx, orc, axis, had, rule):
+    """The SR kernels fold the block scale into the rounding for bf16 input unless the scale
+    exponent is above 16 or below -104; there, elements as small as 2^-133 scale to 2^-150 and
+    below, which round to zero first. 2^18 blocks (8M elements): a wrong bound would show on
+    the ~1 in 65536 elements whose random field is zero."""
+    blocks = fold_boundary_blocks(1 << 18, had, seed=11 + 2 * had + rule)
+    x = blocks.reshape(512, 512 * 32)  # row c: blocks 512c .. 512c + 511
+    if axis == 0:
+        x = x.t().contiguous()  # the same blocks down the columns
+    opts = dict(scale_rule=rule, hadamard=had, sign_mask=0, seed=97)
+    c, s = mx.mx_quantize(x.to(DEV), axis=axis, round=1, **opts)
+    rc, rs = orc.quantize(hostx(x), axis=axis, round_mode=1, nthreads=8, **opts)
+    assert_bytes_equal(s, rs, "scales")
+    assert_bytes_equal(c, rc, "codes")
+
+
 @pytest.mark.parametrize("axis", [1, 0])
 @pytest.mark.parametrize("rnd", [0, 1])
 def test_hadamard_overflow_block(mx, orc, axis, rnd):
