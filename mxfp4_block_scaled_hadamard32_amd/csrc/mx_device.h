@@ -307,8 +307,6 @@ __device__ __forceinline__ void hadamard32_inlane(float (&w)[32]) {
   }
 }
 
-// quant_block32_with takes the stochastic-rounding words from rw_of(d, rw), which fills the
-// converter words of values 8d .. 8d+7.
 // Block maximum of |x| as bits: the unsigned maximum of the raw bits is the largest negative
 // value (if any), the signed maximum the largest positive one (if any); with the sign bits
 // cleared the larger of the two is the largest magnitude, NaN and infinity included.
@@ -325,6 +323,8 @@ __device__ __forceinline__ uint32_t block32_amax_bits(const float (&w)[32]) {
   return max(mu & 0x7FFFFFFFu, (uint32_t)mi & 0x7FFFFFFFu);
 }
 
+// quant_block32_with takes the stochastic-rounding words from rw_of(d, rw), which fills the
+// converter words of values 8d .. 8d+7.
 // FOLD (stochastic rounding of values derived from bf16 input): |x| 2^-e 2^23 is one multiply.
 // It equals |v| 2^23 for v = fl32(x 2^-e) except where that product underflows to zero
 // (|x 2^-e| <= 2^-150), which the fold would round up on a zero field. A nonzero value derived
