@@ -354,21 +354,20 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
 // quantizes them (no lane exchanges in the transform, one scale per lane). A workgroup owns 256
 // rows x 64 CWV columns, with 4 CWV waves: pass p of wave w takes row block 4p + w % 4 of the
 // 64 columns 64 (w / 4).., and lane l column l of those. Lane (q, cg) = (l / 8, l % 8) loads
-// the 8 columns 8cg.. of rows 4q..4q+3 (8 lanes: one
-// 128-byte row) and, for stochastic rounding, computes the Philox words of the same chunk of
-// rows q, q + 8, q + 16, q + 24. The wave's own 4 KiB of LDS holds 32 rows of 128 bytes: first
-// the values, which each lane reads back as the 16-bit entries of its column, then the random
-// fields, stored with the layout of the values they round and read back the same way. Every
-// access of the area covers whole 128-byte rows (no bank conflicts). A lane keeps the codes and
-// scales of its two passes in registers; once all waves are done with their areas, the same
-// 16 CWV KiB hold the code tile for the store phase. With at most 64 registers and 16 KiB of
-// LDS per four waves, eight waves share a SIMD. Measured on a 16384x28672 tensor (Hadamard,
-// ceil, SR, CWV = 1):
-// 128-column tiles with two columns per lane (128 registers, four waves per SIMD) 286-291 us;
-// this kernel with the code tile beside the exchange areas (26 KiB, six waves) 264-266 us; as
-// it stands 259-266 us. Code bytes stored straight from the lanes (16 bytes per line per store)
-// were 20-30% slower. With nearest-even rounding the 8192x14336 Hadamard case took 58.6 us with
-// the 8x8-patch kernel below and 54.8-55.4 us here.
+// the 8 columns 8cg.. of rows 4q..4q+3 (8 lanes: one 128-byte row) and, for stochastic
+// rounding, computes the Philox words of the same chunk of rows q, q + 8, q + 16, q + 24.
+// The wave's own 4 KiB of LDS holds 32 rows of 128 bytes: first the values, which each lane
+// reads back as the 16-bit entries of its column, then the random fields, stored with the
+// layout of the values they round and read back the same way. Every access of the area covers
+// whole 128-byte rows (no bank conflicts). A lane keeps the codes and scales of its two passes
+// in registers; once all waves are done with their areas, the same 16 CWV KiB hold the code
+// tile for the store phase. With at most 64 registers and 16 KiB of LDS per four waves, eight
+// waves share a SIMD. Measured on a 16384x28672 tensor (Hadamard, ceil, SR, CWV = 1): 128-column
+// tiles with two columns per lane (128 registers, four waves per SIMD) 286-291 us; this kernel
+// with the code tile beside the exchange areas (26 KiB, six waves) 264-266 us; as it stands
+// 259-266 us (247 us with the scale fold). Code bytes stored straight from the lanes (16 bytes
+// per line per store) were 20-30% slower. With nearest-even rounding the 8192x14336 Hadamard
+// case took 58.6 us with the 8x8-patch kernel below and 54.8-55.4 us here.
 // ---------------------------------------------------------------------------------------------
 constexpr int kColLaneTileCols = 64;
 
