@@ -88,3 +88,21 @@ def test_gemm_output_past_2g_elements(mx, orc):
     check_gemm(out, C, Cabs, rows=rows, cols=cols)
     del out
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("axis,rnd", [(0, 1), (0, 0), (1, 1)])
+def test_quantize_leading_dimension_past_2g_bytes(mx, orc, axis, rnd):
+    """A 32 x 64 slice of a tensor with 2^26 + 64 columns: the loads of row 28 start 3.5 GiB past
+    the first (the column kernels' per-lane offsets, the row kernel's direct loads)."""
+    ld = 2 ** 26 + 64
+    full = torch.empty((32, ld), dtype=torch.bfloat16, device=DEV)
+    src = wl.student_t3((32, 64), seed=81).to(torch.bfloat16)
+    full[:, :64] = src.to(DEV)
+    x = full[:, :64]
+    c, s = mx.mx_quantize(x, axis=axis, round=rnd, **OPTS)
+    torch.cuda.synchronize()
+    rc, rs = orc.quantize(wl.host_input(src), axis=axis, round_mode=rnd, **OPTS)
+    assert_bytes_equal(s, rs, "scales")
+    assert_bytes_equal(c, rc, "codes")
+    del full
+    torch.cuda.empty_cache()
