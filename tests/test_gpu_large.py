@@ -106,3 +106,20 @@ def test_quantize_leading_dimension_past_2g_bytes(mx, orc, axis, rnd):
     assert_bytes_equal(c, rc, "codes")
     del full
     torch.cuda.empty_cache()
+
+
+def test_quantize_mxfp8_columns_leading_dimension_past_2g_bytes(mx, orc):
+    """The MXFP8 column kernel on the same 32 x 64 slice of a 2^26 + 64-column tensor."""
+    ld = 2 ** 26 + 64
+    full = torch.empty((32, ld), dtype=torch.bfloat16, device=DEV)
+    src = wl.student_t3((32, 64), seed=82).to(torch.bfloat16)
+    full[:, :64] = src.to(DEV)
+    c, s = mx.mx_quantize_mxfp8(full[:, :64], fmt=0, axis=0, scale_rule=1, round=1, hadamard=1,
+                                sign_mask=0x2C6FE9B1, seed=99)
+    torch.cuda.synchronize()
+    rc, rs = orc.quantize_fp8(wl.host_input(src), fmt=0, axis=0, scale_rule=1, round_mode=1,
+                              hadamard=1, sign_mask=0x2C6FE9B1, seed=99)
+    assert_bytes_equal(s, rs, "scales")
+    assert_bytes_equal(c, rc, "codes")
+    del full
+    torch.cuda.empty_cache()
