@@ -362,7 +362,8 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
 // whole 128-byte rows (no bank conflicts). A lane keeps the codes and scales of its two passes
 // in registers; once all waves are done with their areas, the same 16 CWV KiB hold the code
 // tile for the store phase. With at most 64 registers and 16 KiB of LDS per four waves, eight
-// waves share a SIMD. Measured on a 16384x28672 tensor (Hadamard, ceil, SR, CWV = 1): 128-column
+// waves share a SIMD (stochastic rounding without the transform needs 75 registers: six waves,
+// 2-11% faster than seven with 3 spilled). Measured on a 16384x28672 tensor (Hadamard, ceil, SR, CWV = 1): 128-column
 // tiles with two columns per lane (128 registers, four waves per SIMD) 286-291 us; this kernel
 // with the code tile beside the exchange areas (26 KiB, six waves) 264-266 us; as it stands
 // 259-266 us (247 us with the scale fold). Code bytes stored straight from the lanes (16 bytes
@@ -378,7 +379,7 @@ __device__ __forceinline__ void wave_sync() {
 }
 
 template <bool HAD, bool SR, bool CEIL, int CWV>
-__global__ __launch_bounds__(kThreads * CWV) __attribute__((amdgpu_waves_per_eu(HAD || !SR ? 8 : 7, 8)))
+__global__ __launch_bounds__(kThreads * CWV) __attribute__((amdgpu_waves_per_eu(HAD || !SR ? 8 : 6, 8)))
 void quant_cols_bf16_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, uint32_t sign_mask,
     uint64_t seed, uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t, int64_t n_rt,
@@ -949,9 +950,11 @@ __global__ __launch_bounds__(kThreads) void quant_cols_fp8_kernel(
 // MXFP8 down the columns of a bf16 tensor with the whole-column kernel's layout: a workgroup
 // owns 256 rows x 64 columns, lane l the 32-row column l of a row block, whose 32 code bytes
 // (two 16-byte pieces) stay in registers over the two passes; after them the same LDS holds the
-// code tile (256 bytes per column, 272-byte stride) for 256-byte stores.
+// code tile (256 bytes per column, 272-byte stride) for 256-byte stores. Stochastic rounding
+// without the transform needs 75 registers and runs at six waves per SIMD: at eight, the 15
+// registers spilled to scratch made it 18% slower on a 16384x8192 tensor.
 template <int FMT, bool HAD, bool SR, bool CEIL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HAD || !SR ? 8 : 6, 8)))
 void quant_cols_fp8_bf16_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, uint32_t sign_mask,
     uint64_t seed, uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t, int64_t n_rt,
