@@ -245,3 +245,34 @@ def test_llama70b_gemm_fp32_full_k(mx, orc, llama70b, gemm):
     torch.cuda.synchronize()
     check_gemm_sampled(orc, o, *L.buf[a], 1, *L.buf[b], 1, L.alpha[gemm], seed=7 + len(gemm),
                        nrows=16, ncols=1024)
+
+
+@pytest.mark.parametrize("src", ["X", "dY"])
+@pytest.mark.parametrize("rule", [1, 0])
+def test_llama70b_columns_sr_without_transform_sampled(mx, orc, llama70b, src, rule):
+    """Stochastic rounding without the transform down the columns (T) of the full-size 70B
+    operands (H 16384x28672, dY 16384x8192): the column kernel's six-waves-per-SIMD variant."""
+    L = llama70b
+    x = getattr(L, src)
+    c, s = mx.mx_quantize(x, axis=0, scale_rule=rule, round=1, hadamard=0, seed=4321)
+    torch.cuda.synchronize()
+    check_quant_rows(orc, x, c, s, 0, row_samples(x.shape[0], count=2, seed=11),
+                     scale_rule=rule, round_mode=1, hadamard=0, seed=4321)
+    del c, s
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_mxfp8_columns_sr_without_transform_sampled(mx, orc, llama70b, fmt):
+    """MXFP8 (E4M3, E5M2) with stochastic rounding and no transform down the columns of the
+    full-size 16384x8192 dY: the MXFP8 column kernel's six-waves-per-SIMD variant, on sampled
+    row ranges."""
+    x = llama70b.dY
+    c, s = mx.mx_quantize_mxfp8(x, fmt=fmt, axis=0, scale_rule=1, round=1, hadamard=0, seed=77)
+    torch.cuda.synchronize()
+    xh = wl.host_input(x)
+    for r0, r1 in row_samples(x.shape[0], count=2, seed=12):
+        rc, rs = orc.quantize_fp8(xh, fmt=fmt, axis=0, scale_rule=1, round_mode=1, hadamard=0,
+                                  seed=77, row_range=(r0, r1))
+        assert_bytes_equal(s[:, r0 // 32:r1 // 32], rs[:, r0 // 32:r1 // 32], f"scales_t {r0}:{r1}")
+        assert_bytes_equal(c[:, r0:r1], rc[:, r0:r1], f"codes_t {r0}:{r1}")
+    del c, s
